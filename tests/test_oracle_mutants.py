@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and
+check that the pins catch every one of them."""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from tests import oracle_pins
+
+# (name, text in mfr_oracle.cpp, replacement)
+MUTANTS = [
+    ("drop_shared", "bf16_bits_to_double(shared_out[t * H + h]) +", ""),
+    ("residual_sign", "bf16_bits_to_double(residual[t * H + h]);",
+     "(-bf16_bits_to_double(residual[t * H + h]));"),
+    ("perm_transposed", "perm_idx[t * K + k]", "perm_idx[k * T + t]"),
+    ("weight_slot_reversed", "topk_w[t * K + k]", "topk_w[t * K + (K - 1 - k)]"),
+    ("eps_outside_root", "std::sqrt(mean_sq + eps_d)", "(std::sqrt(mean_sq) + eps_d)"),
+    ("sum_not_mean", "sumsq / static_cast<double>(H)", "sumsq"),
+    ("gamma_plus_one", "* bf16_bits_to_double(gamma[h])", "* (1.0 + bf16_bits_to_double(gamma[h]))"),
+    ("scale_dropped", "scale_d * routed[h]", "routed[h]"),
+    ("norm_of_rounded_numerator", "s[h] / denom", "bf16_bits_to_double(rne_bf16_from_f64(s[h])) / denom"),
+    ("norm_of_rounded_sumsq", "sumsq += s[h] * s[h];",
+     "{ const double q = bf16_bits_to_double(rne_bf16_from_f64(s[h])); sumsq += q * q; }"),
+    ("round_after_shared_add",
+     "s[h] = scale_d * routed[h] + bf16_bits_to_double(shared_out[t * H + h]) +",
+     "s[h] = bf16_bits_to_double(rne_bf16_from_f64(scale_d * routed[h] + "
+     "bf16_bits_to_double(shared_out[t * H + h]))) +"),
+    ("zero_index_masked", "if (idx < 0) continue;", "if (idx <= 0) continue;"),
+    ("ties_up", "r = (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "r = fl + 1.0;"),
+    ("subnormals_flushed", "if (lead < -126) lead = -126;", "if (lead < -126) return sign;"),
+    ("truncate_not_round", "if (frac > 0.5) {", "if (frac > 2.0) {"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle_build.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new)
+    path = os.path.join(tmp_path, f"{name}.cpp")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle_build.compile_source(path, os.path.join(tmp_path, f"lib{name}.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught the mutant {name}"
