@@ -1,0 +1,387 @@
+#!/usr/bin/env python
+"""Benchmark of the fused MoE finalize + residual add + RMSNorm on one MI355X.
+
+One step = one call of the fused op over one batch of synthetic input (all of
+its steps: gather, weighted sum, shared and residual adds, rounding, RMSNorm).
+The headline workload is the 8192-token prefill chunk (H=6144, K=8, scale 2.5,
+1% of residual rows x100; 1.21 GB per call, larger than the 256 MB Infinity
+Cache, so every call streams from HBM). Inputs are resident in HBM before the
+timed region; HIP events on the launch stream bracket exactly --steps calls.
+
+Printed (stdout, one JSON line): effective HBM GB/s = algorithmic bytes per
+call / time per call, the roofline object for the fused kernel, the oracle's
+CPU baseline on the same workload, and, as context, decode-latency figures for
+T = 1..64 and the 512-token batch, plus a measured copy ceiling.
+
+Modes used with rocprofv3 (see profiles/):
+  --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
+                     size, for counter collection (FETCH_SIZE / WRITE_SIZE)
+  --summarize-stats  turn a rocprofv3 kernel_stats.csv into a profiles/ summary
+  --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused MoE-finalize+RMSNorm µs/call and effective HBM GB/s (% of peak), 1 MI355X"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+FUSED_KERNEL_PREFIX = "mfr_"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stream_kernel_prefill_T8192.json")
+HEADLINE_CFG, HEADLINE_T = 4, 8192
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "top_finalize_residual_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# device helpers
+# ---------------------------------------------------------------------------
+
+def to_device(d):
+    import numpy as np
+    import torch
+
+    def bf16(u):
+        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).cuda()
+    return dict(expert_out=bf16(d["expert_out"]), perm_idx=torch.from_numpy(d["perm_idx"]).cuda(),
+                topk_w=torch.from_numpy(d["topk_w"]).cuda(), shared_out=bf16(d["shared_out"]),
+                residual=bf16(d["residual"]), gamma=bf16(d["gamma"]))
+
+
+def make_caller(dd, eps, scale):
+    """A zero-allocation closure that enqueues one fused call on the current stream."""
+    import torch
+    import top_finalize_residual_amd as mfr
+    T, K = dd["perm_idx"].shape
+    H = dd["gamma"].shape[0]
+    r_out = torch.empty_like(dd["residual"])
+    n_out = torch.empty_like(dd["residual"])
+    args = [dd[k].data_ptr() for k in ("expert_out", "perm_idx", "topk_w", "shared_out",
+                                       "residual", "gamma")]
+    ro, no = r_out.data_ptr(), n_out.data_ptr()
+
+    def call():
+        s = torch.cuda.current_stream().cuda_stream
+        rc = mfr.moe_finalize_rmsnorm_raw(*args, eps, scale, ro, no, T, H, K, s)
+        if rc != 0:
+            raise RuntimeError(mfr.strerror(rc))
+    return call, (r_out, n_out)
+
+
+def time_calls(calls, n, warmup):
+    """Mean device ms per call over n calls (events on the launch stream)."""
+    import torch
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(n):
+        calls[i % len(calls)]()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def time_graph(call, per_graph, replays):
+    """Mean device ms per call inside a captured graph of per_graph calls."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(replays):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (per_graph * replays)
+
+
+def copy_ceiling_gbs(nbytes=1 << 30, reps=10):
+    """Read+write GB/s of the plain copy probe on a 1 GiB buffer."""
+    import ctypes
+    import torch
+    from top_finalize_residual_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.mfr_copy_probe.restype = ctypes.c_int
+    lib.mfr_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def call():
+        rc = lib.mfr_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, cus * 8,
+                                torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError("copy probe failed")
+    ms = time_calls([call], reps, 2)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9, call
+
+
+# ---------------------------------------------------------------------------
+# modes
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(d, passes=3):
+    """The oracle as it stands (single-threaded fp64 C++) on the same workload."""
+    import oracle
+    import synth
+    nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    oracle.default()
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        oracle.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
+                                d["residual"], d["gamma"], d["eps"], d["scale"], want_exact=False)
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(nbytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {d['T']}-token workload, {passes} passes, single thread "
+                      f"({dt:.1f} s; {dt / passes * 1e6:.0f} µs/call; host: {cpu}, "
+                      f"{os.cpu_count()} logical CPUs)"}
+
+
+def traffic_for_headline():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def decode_latency():
+    """Per-call device µs at the decode sizes (context figures)."""
+    import synth
+    out = {}
+    for T in synth.CONFIGS[1]["Ts"]:
+        d = synth.config_inputs(1, T)
+        dd = to_device(d)
+        call, _ = make_caller(dd, d["eps"], d["scale"])
+        eager = time_calls([call], 200, 20) * 1e3
+        graph = time_graph(call, 100, 5) * 1e3
+        out[f"T{T}"] = {"graph_us": round(graph, 2), "stream_us": round(eager, 2)}
+    return out
+
+
+def graph_ceiling_batch():
+    """The 512-token batch: cold (8 rotating buffer sets, 604 MB > Infinity
+    Cache) and warm (one set back to back)."""
+    import synth
+    d = synth.config_inputs(3, 512)
+    nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    sets = [to_device(d) for _ in range(8)]
+    calls = [make_caller(dd, d["eps"], d["scale"])[0] for dd in sets]
+    cold = time_calls(calls, 400, 16) * 1e3
+    warm = time_calls(calls[:1], 400, 16) * 1e3
+    return {"us_cold": round(cold, 2), "gbs_cold": round(nbytes / (cold * 1e-6) / 1e9, 1),
+            "us_warm": round(warm, 2), "gbs_warm": round(nbytes / (warm * 1e-6) / 1e9, 1),
+            "bytes": nbytes}
+
+
+def run_bench(args):
+    import numpy as np  # noqa: F401
+    import torch
+    import synth
+    import top_finalize_residual_amd as mfr
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log(f"generating the {HEADLINE_T}-token prefill chunk (seeded, synthetic)")
+    d = synth.config_inputs(HEADLINE_CFG, HEADLINE_T)
+    nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    dd = to_device(d)
+    path = mfr.moe_finalize_rmsnorm_path(d["T"], d["H"], d["K"])
+    call, _ = make_caller(dd, d["eps"], d["scale"])
+    log(f"warmup {args.warmup}, timing {args.steps} calls (path {path})")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"{ms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+
+    rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "us_per_call": round(ms * 1e3, 2), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "prefill chunk: T=8192 tokens, H=6144, K=8, scale 2.5, "
+                                  "1% residual rows x100 (1.21 GB per call, HBM-cold)",
+                      "T": d["T"], "H": d["H"], "K": d["K"], "algorithmic_bytes": nbytes,
+                      "path": {1: "token", 2: "stream"}.get(path, "?"),
+                      "parallelism": "single GPU"}}
+    rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                       "traffic": traffic_for_headline()}
+    if not args.no_extras:
+        log("copy ceiling (1 GiB copy probe)")
+        rec["copy_ceiling_gbs"] = round(copy_ceiling_gbs()[0], 1)
+        rec["roofline"]["frac_of_copy_ceiling"] = round(gbs / rec["copy_ceiling_gbs"], 4)
+        log("decode latency sweep T = 1..64 (H=6144, K=8)")
+        rec["decode_latency_us"] = decode_latency()
+        log("512-token batch, cold and warm")
+        rec["batch_512"] = graph_ceiling_batch()
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline on the same workload (single thread)")
+        rec["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(rec), flush=True)
+
+
+def run_pmc(args):
+    """Short run for counter collection: the headline fused call a few times,
+    then one 1 GiB copy of known size."""
+    import torch
+    import synth
+    torch.cuda.set_device(0)
+    d = synth.config_inputs(HEADLINE_CFG, HEADLINE_T)
+    dd = to_device(d)
+    call, _ = make_caller(dd, d["eps"], d["scale"])
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    _, copy = copy_ceiling_gbs(reps=1)
+    log("pmc run done")
+
+
+def summarize_stats(args):
+    rows = list(csv.DictReader(open(args.summarize_stats)))
+    lines = [f"# rocprofv3 kernel statistics: {args.title}", "", "Command:", "",
+             "```", args.command, "```", "",
+             "| kernel | calls | avg µs | min µs | max µs | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name", "")
+        short = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} | "
+                     f"{float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} | "
+                     f"{float(r.get('Percentage', 0)):.2f} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(args):
+    """FETCH_SIZE and WRITE_SIZE per dispatch (KiB), calibrated on the copy."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    fetch = per_kernel(args.fetch_csv, "FETCH_SIZE")
+    write = per_kernel(args.write_csv, "WRITE_SIZE")
+
+    def pick(vals, key):
+        ks = [k for k in vals if key in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {key}")
+        v = vals[ks[0]]
+        return ks[0], sum(v) / len(v)
+    copy_bytes = 1 << 30
+    fk, f_fused = pick(fetch, "mfr_stream_kernel")
+    _, w_fused = pick(write, "mfr_stream_kernel")
+    _, f_copy = pick(fetch, "mfr_copy_probe_kernel")
+    _, w_copy = pick(write, "mfr_copy_probe_kernel")
+    cf = copy_bytes / (f_copy * 1024.0)
+    cw = copy_bytes / (w_copy * 1024.0)
+    import synth
+    d = synth.config_inputs(HEADLINE_CFG, HEADLINE_T)
+    alg = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    traffic = f_fused * 1024.0 * cf + w_fused * 1024.0 * cw
+    out = {"kernel": fk, "source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": f_fused, "write_kib_per_dispatch": w_fused,
+           "copy_probe": {"bytes": copy_bytes, "fetch_kib": f_copy, "write_kib": w_copy,
+                          "fetch_scale": cf, "write_scale": cw},
+           "traffic_bytes_per_launch": round(traffic), "algorithmic_bytes": alg,
+           "traffic_over_algorithmic": traffic / alg, "commands": args.command}
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true", help="skip copy ceiling, decode sweep, 512 batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true")
+    ap.add_argument("--summarize-stats")
+    ap.add_argument("--summarize-pmc", action="store_true")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--out")
+    args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the fused op has no cross-GPU step to time here "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}). Run with --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.pmc_run:
+        return run_pmc(args)
+    return run_bench(args)
+
+
+if __name__ == "__main__":
+    main()

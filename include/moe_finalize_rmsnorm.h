@@ -1,0 +1,120 @@
+/*
+ * moe_finalize_rmsnorm.h - C ABI of the fused MoE finalize + residual add +
+ * RMSNorm for MI355X (gfx950).
+ *
+ * The operation is the tail of a decode MoE layer whose top-k reduction was
+ * left open by the experts (vLLM pull request #62174, "defer the MoE top-k
+ * finalize into the next RMSNorm's fused all-reduce": Overview and Details).
+ * For each token t and hidden index h:
+ *
+ *   routed[h] = sum over slots k with perm_idx[t,k] >= 0 of
+ *               topk_w[t,k] * expert_out[perm_idx[t,k], h]
+ *   s[h]      = (scale * routed[h] + shared_out[t,h]) + residual[t,h]
+ *   residual_out[t,h] = bf16(s[h])                                (one rounding)
+ *   normed_out[t,h]   = bf16(s[h] / sqrt(mean_h(s^2) + eps) * gamma[h])
+ *
+ * The page's fused kernel does the top-k sum, the routed scaling, the shared
+ * add, an all-reduce across tensor-parallel ranks, the residual add and the
+ * RMSNorm in one launch (Details); on one GPU the all-reduce is the identity.
+ * The page also states that the fused kernel accumulates in FP32 and that the
+ * finalize rounds once rather than after each step (Claims, Validation): here
+ * the sum s is kept in fp32 registers, rounded to bf16 only at the two outputs,
+ * and the norm is taken of the unrounded fp32 s.
+ *
+ * Data types and layout (all row-major, contiguous, device memory):
+ *   bf16 tensors are passed as raw 16-bit patterns (uint16_t).
+ *   expert_out   [R, H]  bf16   GEMM2 output rows; R is not passed. Every
+ *                               non-negative perm_idx must be < R (not checked:
+ *                               an index >= R reads out of bounds on the GPU).
+ *   perm_idx     [T, K]  int32  row of expert_out for (token t, slot k);
+ *                               any negative value marks a masked slot, whose
+ *                               row is never read and whose weight is ignored.
+ *   topk_w       [T, K]  fp32   routing weights. A zero weight on a valid index
+ *                               is not a mask: the row is still read.
+ *   shared_out   [T, H]  bf16   shared-expert output
+ *   residual     [T, H]  bf16   residual stream
+ *   gamma        [H]     bf16   RMSNorm weight
+ *   eps                  fp32   >= 0 and finite (inside the square root)
+ *   scale                fp32   finite routed scaling factor; callers whose
+ *                               router folds the factor into topk_w pass 1.0
+ *                               (the page requires the experts' factor to be
+ *                               1.0 in that case: Details)
+ *   residual_out [T, H]  bf16   output; may be exactly equal to residual
+ *                               (in place), must not overlap anything else
+ *   normed_out   [T, H]  bf16   output; must not overlap any other argument
+ *
+ * Limits: 0 <= T <= 2^31-1, 8 <= H <= 16384 with H % 8 == 0, 1 <= K <= 16.
+ * bf16 pointers must be 16-byte aligned; perm_idx and topk_w 4-byte aligned.
+ *
+ * Ownership and ordering: the caller owns every buffer; the library allocates
+ * and frees nothing and keeps no per-call state (the page's consumer frees the
+ * deferred buffers: Details). The work is enqueued on `stream` (NULL = the
+ * device's null stream) and the call returns without synchronising; buffers
+ * must stay valid until the stream has passed the kernel. Calls may be
+ * captured into a HIP graph. Results are deterministic: no atomics, and a
+ * fixed reduction order.
+ *
+ * Errors: every argument check runs on the host before anything is enqueued.
+ * On error nothing is launched and a nonzero status is returned; no exception
+ * crosses the ABI. T == 0 returns MFR_OK without launching (pointers are then
+ * not examined). A failed launch returns MFR_ERR_HIP.
+ */
+#ifndef MOE_FINALIZE_RMSNORM_H
+#define MOE_FINALIZE_RMSNORM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mfr_status {
+    MFR_OK = 0,
+    MFR_ERR_NULL = 1,   /* a required pointer is NULL (T > 0) */
+    MFR_ERR_SHAPE = 2,  /* T, H or K outside the limits above */
+    MFR_ERR_ALIGN = 3,  /* a pointer is not aligned as required */
+    MFR_ERR_ALIAS = 4,  /* outputs overlap inputs or each other (other than residual_out == residual) */
+    MFR_ERR_SCALAR = 5, /* eps < 0, or eps or scale not finite */
+    MFR_ERR_HIP = 6,    /* the HIP runtime refused the launch */
+    MFR_ERR_ARG = 7     /* an invalid value passed to moe_finalize_rmsnorm_force */
+};
+
+enum mfr_path {
+    MFR_PATH_UNSUPPORTED = 0,
+    MFR_PATH_TOKEN = 1,  /* one workgroup per token, grid = T: latency path for small T */
+    MFR_PATH_STREAM = 2  /* persistent workgroups looping over tokens: bandwidth path for large T */
+};
+
+/* The fused op. Definition, layouts, limits and errors: see above. */
+int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
+                         const float* topk_w, const uint16_t* shared_out,
+                         const uint16_t* residual, const uint16_t* gamma,
+                         float eps, float scale,
+                         uint16_t* residual_out, uint16_t* normed_out,
+                         int64_t T, int64_t H, int64_t K, hipStream_t stream);
+
+/* Which kernel moe_finalize_rmsnorm would launch for this shape, taking any
+ * override from moe_finalize_rmsnorm_force into account; MFR_PATH_UNSUPPORTED
+ * if the shape is outside the limits. Pure host function: no HIP call. A
+ * caller can use it to decide, before deferring its finalize, that the fused
+ * op will accept the shape (the page's layers defer only when the fused kernel
+ * will run: Details). T == 0 reports the path a nonzero T would take. */
+int moe_finalize_rmsnorm_path(int64_t T, int64_t H, int64_t K);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* moe_finalize_rmsnorm_strerror(int status);
+
+/* Process-wide launch override for testing and tuning; affects later calls
+ * from every thread. path: 0 = automatic, MFR_PATH_TOKEN or MFR_PATH_STREAM.
+ * vectors_per_thread: 0 = automatic, else 1..4 (16-byte vectors of each row
+ * handled per thread; the workgroup size follows from H). wg_per_cu: 0 =
+ * automatic, else 1..16 (persistent workgroups per compute unit, stream path).
+ * Returns MFR_ERR_ARG for values outside those ranges (nothing changes). */
+int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int wg_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FINALIZE_RMSNORM_H */

@@ -1,0 +1,154 @@
+"""The C ABI on the host: symbols, status codes, path query and argument
+validation. Every call here returns before anything is enqueued on a GPU
+(validation runs on the host first), so these run without a GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+mfr = pytest.importorskip("top_finalize_residual_amd", reason="HIP library not built")
+from top_finalize_residual_amd import binding  # noqa: E402
+
+T, H, K = 4, 2048, 8
+A = 1 << 20  # fake, 16-byte aligned, never dereferenced addresses
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(INCLUDE)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([A-Za-z_]\w*)\s*\(", text, re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
+                 "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared but not exported"
+
+
+def test_strerror_covers_every_status():
+    seen = set()
+    for code in range(0, 8):
+        msg = mfr.strerror(code)
+        assert msg and msg != "unknown status"
+        seen.add(msg)
+    assert len(seen) == 8
+    assert mfr.strerror(99) == "unknown status"
+
+
+def test_path_query():
+    assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_TOKEN
+    assert mfr.moe_finalize_rmsnorm_path(28, 6144, 8) == mfr.PATH_TOKEN
+    assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_STREAM
+    assert mfr.moe_finalize_rmsnorm_path(0, 6144, 8) == mfr.PATH_TOKEN
+    for bad in ((-1, 6144, 8), (4, 6143, 8), (4, 0, 8), (4, 16392, 8), (4, 6144, 0),
+                (4, 6144, 17), (2**31, 6144, 8)):
+        assert mfr.moe_finalize_rmsnorm_path(*bad) == mfr.PATH_UNSUPPORTED, bad
+    assert mfr.moe_finalize_rmsnorm_path(4, 16384, 16) != mfr.PATH_UNSUPPORTED
+    assert mfr.moe_finalize_rmsnorm_path(4, 8, 1) != mfr.PATH_UNSUPPORTED
+
+
+def test_force_overrides_and_validates():
+    try:
+        mfr.moe_finalize_rmsnorm_force(mfr.PATH_STREAM, 0, 0)
+        assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_STREAM
+        mfr.moe_finalize_rmsnorm_force(mfr.PATH_TOKEN, 2, 0)
+        assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
+        for bad in ((3, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 17), (0, 0, -1)):
+            with pytest.raises(mfr.MFRError) as e:
+                mfr.moe_finalize_rmsnorm_force(*bad)
+            assert e.value.status == binding.MFR_ERR_ARG
+        # a rejected override leaves the previous one in place
+        assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
+    finally:
+        mfr.moe_finalize_rmsnorm_force(0, 0, 0)
+    assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_STREAM
+
+
+def _ptrs(**over):
+    """A full set of distinct, aligned fake pointers (no overlaps)."""
+    act = T * H * 2
+    p = dict(expert_out=A, perm_idx=A + 64 * act, topk_w=A + 65 * act, shared_out=A + 66 * act,
+             residual=A + 67 * act, gamma=A + 68 * act, residual_out=A + 69 * act,
+             normed_out=A + 70 * act)
+    p.update(over)
+    return p
+
+
+def call(T_=T, H_=H, K_=K, eps=1e-6, scale=2.5, **over):
+    p = _ptrs(**over)
+    return mfr.moe_finalize_rmsnorm_raw(p["expert_out"], p["perm_idx"], p["topk_w"],
+                                        p["shared_out"], p["residual"], p["gamma"], eps, scale,
+                                        p["residual_out"], p["normed_out"], T_, H_, K_, None)
+
+
+@pytest.mark.parametrize("name", ["expert_out", "perm_idx", "topk_w", "shared_out", "residual",
+                                  "gamma", "residual_out", "normed_out"])
+def test_null_pointer(name):
+    assert call(**{name: None}) == binding.MFR_ERR_NULL
+
+
+@pytest.mark.parametrize("shape", [(-1, H, K), (T, 0, K), (T, 7, K), (T, 2044, K), (T, 16392, K),
+                                   (T, H, 0), (T, H, 17), (T, H, -3), (2**31, H, K)])
+def test_bad_shape(shape):
+    assert call(*shape) == binding.MFR_ERR_SHAPE
+
+
+@pytest.mark.parametrize("name,delta", [("expert_out", 8), ("shared_out", 2), ("residual", 4),
+                                        ("gamma", 8), ("residual_out", 2), ("normed_out", 8),
+                                        ("perm_idx", 2), ("topk_w", 1)])
+def test_misaligned(name, delta):
+    base = _ptrs()[name]
+    assert call(**{name: base + delta}) == binding.MFR_ERR_ALIGN
+
+
+@pytest.mark.parametrize("eps,scale", [(-1e-6, 1.0), (math.nan, 1.0), (math.inf, 1.0),
+                                       (1e-6, math.nan), (1e-6, math.inf), (1e-6, -math.inf)])
+def test_bad_scalars(eps, scale):
+    assert call(eps=eps, scale=scale) == binding.MFR_ERR_SCALAR
+
+
+def test_zero_tokens_is_a_no_op():
+    # T == 0: accepted without launching, pointers are not examined
+    assert mfr.moe_finalize_rmsnorm_raw(None, None, None, None, None, None, 1e-6, 1.0,
+                                        None, None, 0, H, K, None) == binding.MFR_OK
+
+
+def test_shape_checked_before_pointers():
+    assert mfr.moe_finalize_rmsnorm_raw(None, None, None, None, None, None, 1e-6, 1.0,
+                                        None, None, 0, 7, K, None) == binding.MFR_ERR_SHAPE
+
+
+def test_aliasing_rules():
+    p = _ptrs()
+    act = T * H * 2
+    # overlapping outputs
+    assert call(normed_out=p["residual_out"]) == binding.MFR_ERR_ALIAS
+    assert call(normed_out=p["residual_out"] + act - 16) == binding.MFR_ERR_ALIAS
+    # residual_out partially overlapping residual
+    assert call(residual_out=p["residual"] + 16) == binding.MFR_ERR_ALIAS
+    # outputs on top of other inputs
+    for name in ("shared_out", "gamma", "perm_idx", "topk_w", "expert_out"):
+        assert call(residual_out=p[name]) == binding.MFR_ERR_ALIAS, name
+        assert call(normed_out=p[name]) == binding.MFR_ERR_ALIAS, name
+    assert call(normed_out=p["residual"]) == binding.MFR_ERR_ALIAS
+    # in place (residual_out == residual) and touching buffers are accepted: the
+    # GPU tests exercise them, since a call that passes validation launches

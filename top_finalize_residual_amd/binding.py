@@ -1,0 +1,132 @@
+"""Python binding of libmoe_finalize_rmsnorm.so (ctypes; argument marshalling only).
+
+Every step of the op runs in the HIP library. torch supplies device memory and
+the current stream. There is no CPU fallback: if the library is missing,
+importing this module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+MFR_OK = 0
+MFR_ERR_NULL = 1
+MFR_ERR_SHAPE = 2
+MFR_ERR_ALIGN = 3
+MFR_ERR_ALIAS = 4
+MFR_ERR_SCALAR = 5
+MFR_ERR_HIP = 6
+MFR_ERR_ARG = 7
+
+PATH_UNSUPPORTED = 0
+PATH_TOKEN = 1
+PATH_STREAM = 2
+
+LIB_PATH = _build.LIB
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run top_finalize_residual_amd/build.py (hipcc, gfx950) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib.moe_finalize_rmsnorm.restype = ctypes.c_int
+_lib.moe_finalize_rmsnorm.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_float, ctypes.c_float,
+                                      _p, _p, _i64, _i64, _i64, _p]
+_lib.moe_finalize_rmsnorm_path.restype = ctypes.c_int
+_lib.moe_finalize_rmsnorm_path.argtypes = [_i64, _i64, _i64]
+_lib.moe_finalize_rmsnorm_strerror.restype = ctypes.c_char_p
+_lib.moe_finalize_rmsnorm_strerror.argtypes = [ctypes.c_int]
+_lib.moe_finalize_rmsnorm_force.restype = ctypes.c_int
+_lib.moe_finalize_rmsnorm_force.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+
+
+class MFRError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"moe_finalize_rmsnorm: {strerror(status)} (status {status})")
+
+
+def lib():
+    """The loaded ctypes library (for raw-pointer calls)."""
+    return _lib
+
+
+def strerror(status):
+    return _lib.moe_finalize_rmsnorm_strerror(int(status)).decode()
+
+
+def moe_finalize_rmsnorm_path(T, H, K):
+    return _lib.moe_finalize_rmsnorm_path(int(T), int(H), int(K))
+
+
+def moe_finalize_rmsnorm_force(path=0, vectors_per_thread=0, wg_per_cu=0):
+    rc = _lib.moe_finalize_rmsnorm_force(int(path), int(vectors_per_thread), int(wg_per_cu))
+    if rc != MFR_OK:
+        raise MFRError(rc)
+
+
+def moe_finalize_rmsnorm_raw(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
+                             scale, residual_out, normed_out, T, H, K, stream):
+    """Direct C call with integer addresses; returns the status code."""
+    return _lib.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
+                                     float(eps), float(scale), residual_out, normed_out,
+                                     int(T), int(H), int(K), stream)
+
+
+def _check(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
+                         residual_out=None, normed_out=None, stream=None):
+    """Fused MoE finalize + residual add + RMSNorm on the current (or given) stream.
+
+    expert_out [R, H] bf16, perm_idx [T, K] int32 (-1 = masked), topk_w [T, K] fp32,
+    shared_out / residual [T, H] bf16, gamma [H] bf16; eps, scale are floats.
+    residual_out / normed_out ([T, H] bf16) are allocated when not given;
+    residual_out may be `residual` itself. Returns (residual_out, normed_out).
+    """
+    _check(expert_out, "expert_out", torch.bfloat16, 2)
+    _check(perm_idx, "perm_idx", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(shared_out, "shared_out", torch.bfloat16, 2)
+    _check(residual, "residual", torch.bfloat16, 2)
+    _check(gamma, "gamma", torch.bfloat16, 1)
+    T, K = perm_idx.shape
+    H = gamma.shape[0]
+    if expert_out.shape[1] != H:
+        raise ValueError("expert_out width differs from gamma length")
+    for name, t in (("shared_out", shared_out), ("residual", residual)):
+        if tuple(t.shape) != (T, H):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(T, H)}")
+    if tuple(topk_w.shape) != (T, K):
+        raise ValueError("topk_w shape differs from perm_idx shape")
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=residual.device)
+    if normed_out is None:
+        normed_out = torch.empty((T, H), dtype=torch.bfloat16, device=residual.device)
+    _check(residual_out, "residual_out", torch.bfloat16, 2)
+    _check(normed_out, "normed_out", torch.bfloat16, 2)
+    if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
+        raise ValueError("outputs must be [T, H]")
+    if stream is None:
+        stream = torch.cuda.current_stream(residual.device)
+    rc = _lib.moe_finalize_rmsnorm(
+        expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
+        residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale),
+        residual_out.data_ptr(), normed_out.data_ptr(), T, H, K, stream.cuda_stream)
+    if rc != MFR_OK:
+        raise MFRError(rc)
+    return residual_out, normed_out

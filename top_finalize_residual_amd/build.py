@@ -1,0 +1,51 @@
+"""Build the HIP library (libmoe_finalize_rmsnorm.so) in-tree for gfx950.
+
+The library is compiled with hipcc straight from csrc/ and placed next to
+this file, where the Python binding loads it. Flags:
+  --offload-arch=gfx950          CDNA4 (MI355X) code only
+  -ffp-contract=off              every FMA in the kernels is written out
+  -target-feature -packed-fp32-ops  no packed fp32 VALU ops are emitted
+"""
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmoe_finalize_rmsnorm.so")
+PROBE_LIB = os.path.join(PKG, "libmfr_copy_probe.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+HIPFLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _hipcc(sources, out, verbose=False):
+    cmd = [HIPCC, *HIPFLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out + ".tmp", *sources]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 target feature and says so
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and "(ignoring feature)" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(verbose=False):
+    """Compile the product library and the bench's copy-probe library."""
+    _hipcc([os.path.join(CSRC, "mfr_kernels.hip")], LIB, verbose)
+    _hipcc([os.path.join(CSRC, "copy_probe.hip")], PROBE_LIB, verbose)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

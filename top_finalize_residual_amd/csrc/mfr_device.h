@@ -1,0 +1,81 @@
+// Device helpers for the fused MoE finalize + RMSNorm kernels (gfx950).
+//
+// bf16 handling: a 16-byte vector holds 8 bf16 values as 4 dwords; element
+// 2i sits in the low half of dword i and element 2i+1 in the high half.
+// Widening is exact (a shift or a mask). Narrowing uses the CDNA4 packed
+// convert v_cvt_pk_bf16_f32, which rounds to nearest-even (the default mode),
+// reached through clang's vector conversion to __bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfr {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Two fp32 values -> one dword of two bf16 (round to nearest-even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
+    // e is a compile-time constant after unrolling
+    const uint32_t d = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? bf16_hi(d) : bf16_lo(d);
+}
+
+// Raw buffer access. A descriptor covers [base, base + nbytes); loads at or
+// past nbytes return zero without a memory access and stores there are
+// dropped, so a zero-record descriptor turns a whole row access into a no-op.
+// Word 3 of a gfx9-family raw buffer descriptor selects 32-bit data format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kAuxDefault = 0;
+constexpr int kAuxStream = 2;  // nt: data read once, do not keep it in cache
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(nbytes), kRsrcWord3);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ void buf_store(u32x4 v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, AUX);
+}
+
+// One DPP move of a float within a row of 16 lanes (every lane active).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, returned to every lane. Fixed tree:
+// xor-1 and xor-2 within quads, half-mirror and mirror within rows of 16
+// (DPP, so every lane of a row ends with the row sum), then the four row sums
+// read as scalars and added as (r0 + r1) + (r2 + r3). Deterministic.
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);  // row_half_mirror
+    x += dpp<0x140>(x);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+}  // namespace mfr
