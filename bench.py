@@ -43,8 +43,11 @@ def log(*a):
 
 
 def kernel_source_hash():
+    """Hash of the fused kernel's sources (not the probes): traffic figures
+    measured on an older version of the kernel are not reported."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "top_finalize_residual_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "top_finalize_residual_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "mfr_*"))):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -128,29 +131,43 @@ def time_graph(call, per_graph, replays):
     return e0.elapsed_time(e1) / (per_graph * replays)
 
 
-def copy_ceiling_gbs(nbytes=1 << 30, reps=10):
-    """Read+write GB/s of the plain copy probe on a 1 GiB buffer."""
+def _probe_lib():
     import ctypes
-    import torch
     from top_finalize_residual_amd import build as b
     lib = ctypes.CDLL(b.PROBE_LIB)
-    lib.mfr_copy_probe.restype = ctypes.c_int
-    lib.mfr_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                   ctypes.c_void_p]
+    for fn in (lib.mfr_copy_probe, lib.mfr_read_probe):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                       ctypes.c_void_p]
+    return lib
+
+
+def probe_ceilings(nbytes=1 << 30, reps=10):
+    """GB/s of the copy probe (read + write bytes) and of the read-only probe,
+    on 1 GiB buffers (4x the Infinity Cache, so both stream from HBM)."""
+    import torch
+    lib = _probe_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus * 8
+    sink = torch.empty(grid, dtype=torch.int32, device="cuda")
 
-    def call():
-        rc = lib.mfr_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, cus * 8,
-                                torch.cuda.current_stream().cuda_stream)
-        if rc != 0:
+    def copy():
+        if lib.mfr_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, grid,
+                              torch.cuda.current_stream().cuda_stream) != 0:
             raise RuntimeError("copy probe failed")
-    ms = time_calls([call], reps, 2)
-    del src, dst
+
+    def read():
+        if lib.mfr_read_probe(src.data_ptr(), sink.data_ptr(), nbytes, grid,
+                              torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("read probe failed")
+    copy_gbs = 2 * nbytes / (time_calls([copy], reps, 2) * 1e-3) / 1e9
+    read_gbs = nbytes / (time_calls([read], reps, 2) * 1e-3) / 1e9
+    del src, dst, sink
     torch.cuda.empty_cache()
-    return 2 * nbytes / (ms * 1e-3) / 1e9, call
+    return copy_gbs, read_gbs
 
 
 # ---------------------------------------------------------------------------
@@ -267,9 +284,9 @@ def run_bench(args):
                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                        "traffic": traffic_for_headline()}
     if not args.no_extras:
-        log("copy ceiling (1 GiB copy probe)")
-        rec["copy_ceiling_gbs"] = round(copy_ceiling_gbs()[0], 1)
-        rec["roofline"]["frac_of_copy_ceiling"] = round(gbs / rec["copy_ceiling_gbs"], 4)
+        log("measured ceilings (1 GiB copy and read probes)")
+        cp, rd = probe_ceilings()
+        rec["probe_ceilings_gbs"] = {"copy": round(cp, 1), "read_only": round(rd, 1)}
         log("decode latency sweep T = 1..64 (H=6144, K=8)")
         rec["decode_latency_us"] = decode_latency()
         log("512-token batch, cold and warm")
@@ -292,7 +309,7 @@ def run_pmc(args):
     for _ in range(args.steps):
         call()
     torch.cuda.synchronize()
-    _, copy = copy_ceiling_gbs(reps=1)
+    probe_ceilings(reps=1)
     log("pmc run done")
 
 

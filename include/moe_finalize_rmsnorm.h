@@ -80,10 +80,19 @@ enum mfr_status {
     MFR_ERR_ARG = 7     /* an invalid value passed to moe_finalize_rmsnorm_force */
 };
 
+/* Both paths launch one workgroup per token (grid = T); they differ in launch
+ * shape and store policy. */
 enum mfr_path {
     MFR_PATH_UNSUPPORTED = 0,
-    MFR_PATH_TOKEN = 1,  /* one workgroup per token, grid = T: latency path for small T */
-    MFR_PATH_STREAM = 2  /* persistent workgroups looping over tokens: bandwidth path for large T */
+    MFR_PATH_TOKEN = 1,  /* small T, latency: widest workgroup per token (768 threads at H = 6144) */
+    MFR_PATH_STREAM = 2  /* large T, bandwidth: 256 threads per token, write-through stores once
+                            the outputs outgrow the L2 */
+};
+
+enum mfr_store_policy {
+    MFR_STORE_AUTO = 0,
+    MFR_STORE_WRITE_BACK = 1,
+    MFR_STORE_WRITE_THROUGH = 2
 };
 
 /* The fused op. Definition, layouts, limits and errors: see above. */
@@ -94,7 +103,7 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
                          uint16_t* residual_out, uint16_t* normed_out,
                          int64_t T, int64_t H, int64_t K, hipStream_t stream);
 
-/* Which kernel moe_finalize_rmsnorm would launch for this shape, taking any
+/* Which path moe_finalize_rmsnorm would take for this shape, taking any
  * override from moe_finalize_rmsnorm_force into account; MFR_PATH_UNSUPPORTED
  * if the shape is outside the limits. Pure host function: no HIP call. A
  * caller can use it to decide, before deferring its finalize, that the fused
@@ -108,10 +117,13 @@ const char* moe_finalize_rmsnorm_strerror(int status);
 /* Process-wide launch override for testing and tuning; affects later calls
  * from every thread. path: 0 = automatic, MFR_PATH_TOKEN or MFR_PATH_STREAM.
  * vectors_per_thread: 0 = automatic, else 1..4 (16-byte vectors of each row
- * handled per thread; the workgroup size follows from H). wg_per_cu: 0 =
- * automatic, else 1..16 (persistent workgroups per compute unit, stream path).
- * Returns MFR_ERR_ARG for values outside those ranges (nothing changes). */
-int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int wg_per_cu);
+ * handled per thread; the workgroup size follows from H; a value whose
+ * workgroup would exceed the kernel's limit falls back to automatic).
+ * store_policy: an mfr_store_policy value. residual_out is bit-identical
+ * under every override; normed_out can differ in the last bit between
+ * workgroup shapes, whose sum-of-squares reduction trees differ. Returns
+ * MFR_ERR_ARG for values outside those ranges (nothing changes). */
+int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int store_policy);
 
 #ifdef __cplusplus
 }

@@ -39,8 +39,8 @@ def to_device(d):
 class forced:
     """Context manager: force a launch configuration, restore automatic after."""
 
-    def __init__(self, path=0, vpt=0, wgpcu=0):
-        self.args = (path, vpt, wgpcu)
+    def __init__(self, path=0, vpt=0, store=0):
+        self.args = (path, vpt, store)
 
     def __enter__(self):
         mfr.moe_finalize_rmsnorm_force(*self.args)
@@ -51,9 +51,9 @@ class forced:
         return False
 
 
-def run(dd, eps, scale, path=0, vpt=0, wgpcu=0, residual_out=None, normed_out=None):
+def run(dd, eps, scale, path=0, vpt=0, store=0, residual_out=None, normed_out=None):
     """One call on device tensors; returns host uint16 (residual_out, normed_out)."""
-    with forced(path, vpt, wgpcu):
+    with forced(path, vpt, store):
         r, n = mfr.moe_finalize_rmsnorm(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
                                         dd["shared_out"], dd["residual"], dd["gamma"], eps, scale,
                                         residual_out=residual_out, normed_out=normed_out)

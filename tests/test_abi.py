@@ -58,6 +58,9 @@ def test_path_query():
     assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_TOKEN
     assert mfr.moe_finalize_rmsnorm_path(28, 6144, 8) == mfr.PATH_TOKEN
     assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_STREAM
+    assert mfr.moe_finalize_rmsnorm_path(256, 6144, 8) == mfr.PATH_TOKEN
+    assert mfr.moe_finalize_rmsnorm_path(257, 6144, 8) == mfr.PATH_STREAM
+    assert mfr.moe_finalize_rmsnorm_path(512, 6144, 8) == mfr.PATH_STREAM
     assert mfr.moe_finalize_rmsnorm_path(0, 6144, 8) == mfr.PATH_TOKEN
     for bad in ((-1, 6144, 8), (4, 6143, 8), (4, 0, 8), (4, 16392, 8), (4, 6144, 0),
                 (4, 6144, 17), (2**31, 6144, 8)):
@@ -72,7 +75,7 @@ def test_force_overrides_and_validates():
         assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_STREAM
         mfr.moe_finalize_rmsnorm_force(mfr.PATH_TOKEN, 2, 0)
         assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
-        for bad in ((3, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 17), (0, 0, -1)):
+        for bad in ((3, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 3), (0, 0, -1)):
             with pytest.raises(mfr.MFRError) as e:
                 mfr.moe_finalize_rmsnorm_force(*bad)
             assert e.value.status == binding.MFR_ERR_ARG

@@ -46,10 +46,12 @@ def test_tile_variants(cfg_data, cfg, T, path, vpt):
     gu.check(d, r, n, ref=ref)
 
 
-@pytest.mark.parametrize("wgpcu", [1, 2, 5])
-def test_stream_grid_sizes(cfg_data, wgpcu):
+@pytest.mark.parametrize("store", [mfr.STORE_WRITE_BACK, mfr.STORE_WRITE_THROUGH],
+                         ids=["write_back", "write_through"])
+@pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
+def test_store_policies(cfg_data, path, store):
     d, dd, ref = cfg_data(3, 512)
-    r, n = gu.run(dd, d["eps"], d["scale"], path=mfr.PATH_STREAM, wgpcu=wgpcu)
+    r, n = gu.run(dd, d["eps"], d["scale"], path=path, store=store)
     gu.check(d, r, n, ref=ref)
 
 
@@ -173,6 +175,10 @@ def test_deterministic_and_path_independent():
     for vpt in (1, 2, 4):
         rv, _ = gu.run(dd, d["eps"], d["scale"], path=mfr.PATH_TOKEN, vpt=vpt)
         assert np.array_equal(ra, rv), vpt
+    # the store policy changes only where the bytes go, never their value
+    for store in (mfr.STORE_WRITE_BACK, mfr.STORE_WRITE_THROUGH):
+        rs, ns = gu.run(dd, d["eps"], d["scale"], path=mfr.PATH_STREAM, store=store)
+        assert np.array_equal(ra, rs) and np.array_equal(na, ns), store
 
 
 def test_batch_invariance():

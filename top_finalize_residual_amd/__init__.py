@@ -12,6 +12,9 @@ from .binding import (  # noqa: F401
     PATH_STREAM,
     PATH_TOKEN,
     PATH_UNSUPPORTED,
+    STORE_AUTO,
+    STORE_WRITE_BACK,
+    STORE_WRITE_THROUGH,
     moe_finalize_rmsnorm,
     moe_finalize_rmsnorm_force,
     moe_finalize_rmsnorm_path,

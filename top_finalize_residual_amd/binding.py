@@ -24,6 +24,10 @@ PATH_UNSUPPORTED = 0
 PATH_TOKEN = 1
 PATH_STREAM = 2
 
+STORE_AUTO = 0
+STORE_WRITE_BACK = 1
+STORE_WRITE_THROUGH = 2
+
 LIB_PATH = _build.LIB
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -62,8 +66,9 @@ def moe_finalize_rmsnorm_path(T, H, K):
     return _lib.moe_finalize_rmsnorm_path(int(T), int(H), int(K))
 
 
-def moe_finalize_rmsnorm_force(path=0, vectors_per_thread=0, wg_per_cu=0):
-    rc = _lib.moe_finalize_rmsnorm_force(int(path), int(vectors_per_thread), int(wg_per_cu))
+def moe_finalize_rmsnorm_force(path=0, vectors_per_thread=0, store_policy=0):
+    """Process-wide launch override (0 = automatic for each); see the C header."""
+    rc = _lib.moe_finalize_rmsnorm_force(int(path), int(vectors_per_thread), int(store_policy))
     if rc != MFR_OK:
         raise MFRError(rc)
 

@@ -38,8 +38,16 @@ __device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
 // Word 3 of a gfx9-family raw buffer descriptor selects 32-bit data format.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy bits of a buffer access on gfx950 (sc0 = 1, nt = 2, sc1 = 16).
 constexpr int kAuxDefault = 0;
-constexpr int kAuxStream = 2;  // nt: data read once, do not keep it in cache
+constexpr int kAuxStream = 2;  // nt: data touched once, do not keep it in cache
+constexpr int kAuxSc1 = 16;    // sc1 on a store: system scope, written through the L2
+// Policy per stream of the fused op (chosen by measurement on MI355X).
+constexpr int kAuxRows = kAuxStream;        // gathered expert rows (read once)
+constexpr int kAuxActIn = kAuxStream;       // shared and residual rows (read once)
+constexpr int kAuxGamma = kAuxDefault;      // gamma (re-read by every workgroup)
+constexpr int kAuxOut = kAuxDefault;        // outputs that fit in L2: write-back
+constexpr int kAuxWriteThrough = kAuxSc1;   // outputs larger than L2: write-through
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),

@@ -10,11 +10,12 @@
 // The op is a gather-stream: per token it reads K rows of H bf16 plus the
 // shared and residual rows and writes two rows, about 0.96 flop per byte, so
 // it is bound by HBM bandwidth at large T and by latency at small T. Nothing
-// here is a dense contraction, so no MFMA is used. Both kernels share one
-// per-token body:
-//   * a workgroup owns one token at a time; thread i handles the 16-byte
-//     vectors i, i + NT, ..., i + (VPT-1)*NT of every row it touches, so each
-//     wave instruction moves 1 KiB of one row, fully coalesced;
+// here is a dense contraction, so no MFMA is used.
+//
+// One workgroup owns one token (grid = T):
+//   * thread i handles the 16-byte vectors i, i + NT, ..., i + (VPT-1)*NT of
+//     every row it touches, so each wave instruction moves 1 KiB of one row,
+//     fully coalesced, through raw buffer loads;
 //   * shared, residual and gamma loads are issued first (they do not depend
 //     on the routing), then the K routing indices and weights are read as
 //     wave-uniform scalars and all valid rows' loads are issued together
@@ -25,9 +26,17 @@
 //   * sum of squares: per lane, then a DPP tree within each wave, then one
 //     LDS step across waves behind a single barrier;
 //   * normalisation from the registers still holding s (no second read).
-// The token kernel (grid = T) is the latency path; the stream kernel runs a
-// persistent grid sized to the device's occupancy that walks the tokens, for
-// large T.
+// Two launch shapes ("paths") of the same kernel:
+//   * token path (small T, latency): the widest workgroup, one 16-byte vector
+//     per thread per row (768 threads at H = 6144), so the K row loads of a
+//     lone token are spread over as many waves as possible;
+//   * stream path (large T, bandwidth): 256 threads per token (3 vectors per
+//     thread per row at H = 6144), so three tokens are resident per CU, and,
+//     once the outputs outgrow the L2, write-through stores (sc1) that send
+//     them straight on instead of through L2 write-back.
+// A persistent variant (a grid sized to the CUs, each workgroup looping over
+// tokens) measured 3-4% slower than this grid of tokens at T = 512 and 8192:
+// the hardware dispatcher balances the tail better than a static assignment.
 
 #include "mfr_device.h"
 #include "moe_finalize_rmsnorm.h"
@@ -57,29 +66,33 @@ struct Params {
 
 constexpr int MAX_WAVES = 16;  // 1024 threads
 
-// Loads the rows of slots [k0, k0 + 8) and folds them into acc in slot order.
-// Straight-line code: the scalar index/weight loads, then all eight row loads,
-// then the FMAs. A masked slot (index < 0) or a slot at or past K gets a
-// zero-record descriptor and a zero weight: its loads return zeros without
-// touching memory and its FMA adds +0, which leaves acc bit-for-bit unchanged
-// (acc starts at +0 and an exact-zero sum rounds to +0). No branches.
-template <int VPT, bool CHECK_K>
-__device__ __forceinline__ void gather8(const Params& p, const int32_t* prow, const float* wrow,
-                                        int k0, const uint32_t (&off)[VPT],
-                                        float (&acc)[VPT][8]) {
-    const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
-    // Both metadata arrays are read unconditionally (eight scalar loads each,
-    // merged by the compiler), then the slot decisions are uniform selects.
-    int32_t idx[8];
-    float wr[8];
+// Routing metadata of slots [k0, k0 + 8): indices and weights, read
+// unconditionally (wave-uniform scalar loads, merged by the compiler). With
+// CHECK_K, slots at or past K re-read slot K-1 so every load stays in bounds;
+// gather_rows8 ignores them.
+template <bool CHECK_K>
+__device__ __forceinline__ void load_meta8(const Params& p, const int32_t* prow, const float* wrow,
+                                           int k0, int32_t (&idx)[8], float (&wr)[8]) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-        // CHECK_K: clamp to a slot that exists so the scalar load stays in bounds.
         const int k = k0 + kk;
         const int kc = CHECK_K ? (k < p.K ? k : p.K - 1) : k;
         idx[kk] = prow[kc];
         wr[kk] = wrow[kc];
     }
+}
+
+// Loads the rows of slots [k0, k0 + 8) and folds them into acc in slot order.
+// Straight-line code: all eight row loads are issued, then the FMAs. A masked
+// slot (index < 0) or a slot at or past K gets a zero-record descriptor and a
+// zero weight: its loads return zeros without touching memory and its FMA
+// adds +0, which leaves acc bit-for-bit unchanged (acc starts at +0 and an
+// exact-zero sum rounds to +0). No branches.
+template <int VPT, bool CHECK_K>
+__device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&idx)[8],
+                                             const float (&wr)[8], int k0,
+                                             const uint32_t (&off)[VPT], float (&acc)[VPT][8]) {
+    const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
     rsrc_t rows[8];
     float w[8];
 #pragma unroll
@@ -94,7 +107,7 @@ __device__ __forceinline__ void gather8(const Params& p, const int32_t* prow, co
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) r[kk][j] = buf_load<kAuxStream>(rows[kk], off[j]);
+        for (int j = 0; j < VPT; ++j) r[kk][j] = buf_load<kAuxRows>(rows[kk], off[j]);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -110,7 +123,7 @@ __device__ __forceinline__ void gather8(const Params& p, const int32_t* prow, co
 // every row; offsets at or past the row end (a ragged last tile) fall outside
 // the descriptors' range, so their loads return zero and their stores are
 // dropped by the hardware.
-template <int VPT, int KT>
+template <int VPT, int KT, int OUT_AUX>
 __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t, float* red) {
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
@@ -121,17 +134,29 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
 #pragma unroll
     for (int j = 0; j < VPT; ++j) off[j] = static_cast<uint32_t>(tid + j * nt) * 16u;
 
-    // Inputs that do not depend on the routing go first.
+    // Order of issue: the routing metadata (scalar loads), then the loads that
+    // do not depend on it (shared, residual, gamma), and only then anything
+    // that waits for the metadata. The scheduling barrier keeps the compiler
+    // from sinking those independent loads below the metadata wait, so every
+    // workgroup starts streaming HBM one memory latency earlier.
+    constexpr bool CHECK_K = KT != 8;
+    const int32_t* prow = p.perm_idx + t * p.K;
+    const float* wrow = p.topk_w + t * p.K;
+    int32_t idx[8];
+    float wr[8];
+    load_meta8<CHECK_K>(p, prow, wrow, 0, idx, wr);
+
     const rsrc_t sh_r = make_rsrc(p.shared_out + trow, rowbytes);
     const rsrc_t rs_r = make_rsrc(p.residual + trow, rowbytes);
     const rsrc_t gm_r = make_rsrc(p.gamma, rowbytes);
     u32x4 sh[VPT], rs[VPT], gm[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-        sh[j] = buf_load<kAuxStream>(sh_r, off[j]);
-        rs[j] = buf_load<kAuxStream>(rs_r, off[j]);
-        gm[j] = buf_load<kAuxDefault>(gm_r, off[j]);
+        sh[j] = buf_load<kAuxActIn>(sh_r, off[j]);
+        rs[j] = buf_load<kAuxActIn>(rs_r, off[j]);
+        gm[j] = buf_load<kAuxGamma>(gm_r, off[j]);
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[VPT][8];
 #pragma unroll
@@ -139,13 +164,10 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
 
-    const int32_t* prow = p.perm_idx + t * p.K;
-    const float* wrow = p.topk_w + t * p.K;
-    if (KT == 8) {
-        gather8<VPT, false>(p, prow, wrow, 0, off, acc);
-    } else {
-        gather8<VPT, true>(p, prow, wrow, 0, off, acc);
-        if (p.K > 8) gather8<VPT, true>(p, prow, wrow, 8, off, acc);
+    gather_rows8<VPT, CHECK_K>(p, idx, wr, 0, off, acc);
+    if (CHECK_K && p.K > 8) {
+        load_meta8<true>(p, prow, wrow, 8, idx, wr);
+        gather_rows8<VPT, true>(p, idx, wr, 8, off, acc);
     }
 
     // s = (routed + shared) + residual; residual_out = bf16(s); per-lane sum of squares.
@@ -163,7 +185,7 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
         o.y = pack_bf16x2(acc[j][2], acc[j][3]);
         o.z = pack_bf16x2(acc[j][4], acc[j][5]);
         o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-        buf_store<kAuxDefault>(o, ro_r, off[j]);
+        buf_store<OUT_AUX>(o, ro_r, off[j]);
     }
 
     // Row reduction: wave tree, then the waves' partial sums in order.
@@ -186,7 +208,7 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
         o.y = pack_bf16x2(y[2], y[3]);
         o.z = pack_bf16x2(y[4], y[5]);
         o.w = pack_bf16x2(y[6], y[7]);
-        buf_store<kAuxDefault>(o, no_r, off[j]);
+        buf_store<OUT_AUX>(o, no_r, off[j]);
     }
 }
 
@@ -197,29 +219,18 @@ struct Bound {
     static constexpr int kThreads = VPT == 1 ? 1024 : 512;
 };
 
-template <int VPT, int KT>
-__global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_token_kernel(Params p) {
+// One workgroup per token. OUT_AUX is the cache policy of the two output
+// stores (write-back, or write-through for outputs larger than the L2).
+template <int VPT, int KT, int OUT_AUX>
+__global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(Params p) {
     __shared__ float red[MAX_WAVES];
-    finalize_token<VPT, KT>(p, static_cast<int64_t>(blockIdx.x), red);
-}
-
-template <int VPT, int KT>
-__global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_stream_kernel(Params p) {
-    // Two reduction slots, alternated per token: a wave can only reach the
-    // token after next once every wave has passed the next token's barrier,
-    // i.e. after everyone has finished reading this token's slot.
-    __shared__ float red[2][MAX_WAVES];
-    int par = 0;
-    for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
-        finalize_token<VPT, KT>(p, t, red[par]);
-        par ^= 1;
-    }
+    finalize_token<VPT, KT, OUT_AUX>(p, static_cast<int64_t>(blockIdx.x), red);
 }
 
 }  // namespace mfr
 
 // ---------------------------------------------------------------------------
-// Host side: validation, path choice, launch.
+// Host side: validation, launch shape, launch.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -227,16 +238,18 @@ constexpr int64_t kHMax = 16384;
 constexpr int64_t kKMax = 16;
 constexpr int64_t kTMax = 2147483647;
 constexpr int kVptMax = 4;
-// Token counts up to this use the one-workgroup-per-token kernel.
+// Token counts up to this use the token path (widest workgroup per token).
+// Measured on MI355X at H = 6144: the token path is ahead up to T = 256, the
+// 256-thread stream shape from T = 512.
 constexpr int64_t kTokenPathMaxT = 256;
-constexpr int kMaxDevices = 64;
+// Output bytes (both outputs) from which the stores write through. Measured on
+// MI355X at H = 6144: write-back wins at T = 512 (12.6 MB of outputs, which
+// the 32 MB of L2 absorbs), write-through from T = 1024 (25 MB) up.
+constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
 
 std::atomic<int> g_force_path{0};
 std::atomic<int> g_force_vpt{0};
-std::atomic<int> g_force_wgpcu{0};
-std::atomic<int> g_cu_count[kMaxDevices];
-// occupancy cache: [device][vpt-1][threads/64 - 1]
-std::atomic<int> g_occ[kMaxDevices][kVptMax][2][16];
+std::atomic<int> g_force_store{0};
 
 int max_threads(int vpt) { return vpt == 1 ? 1024 : 512; }
 
@@ -257,21 +270,25 @@ int choose_path(int64_t T) {
 }
 
 // Vectors per thread: the token path spreads a row over as many threads as
-// possible (latency); the stream path uses up to 256 threads per token so that
-// more tokens are resident per CU (bandwidth).
+// possible (latency); the stream path uses at most 256 threads per token so
+// that more tokens are resident per CU (bandwidth).
 int choose_vpt(int path, int64_t V) {
     const int f = g_force_vpt.load(std::memory_order_relaxed);
     if (f >= 1 && f <= kVptMax && threads_for(V, f) <= max_threads(f)) return f;
-    if (path == MFR_PATH_TOKEN) {
-        for (int v = 1; v <= kVptMax; ++v)
-            if (threads_for(V, v) <= max_threads(v)) return v;
-    } else {
+    if (path == MFR_PATH_STREAM) {
         for (int v = 1; v <= kVptMax; ++v)
             if (threads_for(V, v) <= 256) return v;
-        for (int v = 1; v <= kVptMax; ++v)
-            if (threads_for(V, v) <= max_threads(v)) return v;
     }
+    for (int v = 1; v <= kVptMax; ++v)
+        if (threads_for(V, v) <= max_threads(v)) return v;
     return kVptMax;
+}
+
+bool write_through(int path, int64_t T, int64_t H) {
+    const int f = g_force_store.load(std::memory_order_relaxed);
+    if (f == MFR_STORE_WRITE_BACK) return false;
+    if (f == MFR_STORE_WRITE_THROUGH) return true;
+    return path == MFR_PATH_STREAM && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes;
 }
 
 bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
@@ -281,53 +298,25 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Kernel address for (path, vectors per thread, K == 8).
+template <int VPT, int KT>
+const void* pick_store(bool wt) {
+    return wt ? reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough>)
+              : reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut>);
+}
+
 template <int VPT>
-const void* pick(int path, bool k8) {
-    if (path == MFR_PATH_TOKEN)
-        return k8 ? reinterpret_cast<const void*>(&mfr::mfr_token_kernel<VPT, 8>)
-                  : reinterpret_cast<const void*>(&mfr::mfr_token_kernel<VPT, 0>);
-    return k8 ? reinterpret_cast<const void*>(&mfr::mfr_stream_kernel<VPT, 8>)
-              : reinterpret_cast<const void*>(&mfr::mfr_stream_kernel<VPT, 0>);
+const void* pick(bool k8, bool wt) {
+    return k8 ? pick_store<VPT, 8>(wt) : pick_store<VPT, 0>(wt);
 }
 
-const void* kernel_for(int path, int vpt, bool k8) {
+// Kernel address for (vectors per thread, K == 8, write-through outputs).
+const void* kernel_for(int vpt, bool k8, bool wt) {
     switch (vpt) {
-        case 1: return pick<1>(path, k8);
-        case 2: return pick<2>(path, k8);
-        case 3: return pick<3>(path, k8);
-        default: return pick<4>(path, k8);
+        case 1: return pick<1>(k8, wt);
+        case 2: return pick<2>(k8, wt);
+        case 3: return pick<3>(k8, wt);
+        default: return pick<4>(k8, wt);
     }
-}
-
-// Persistent grid size for the stream kernel: compute units times resident
-// workgroups per CU (from the occupancy calculator, cached per device).
-hipError_t stream_grid(const void* kern, int vpt, int variant, int nt, int64_t T, int64_t* grid) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
-    if (cus <= 0) {
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        g_cu_count[dev].store(cus, std::memory_order_relaxed);
-    }
-    int per_cu = g_force_wgpcu.load(std::memory_order_relaxed);
-    if (per_cu <= 0) {
-        const int slot = nt / 64 - 1;
-        per_cu = g_occ[dev][vpt - 1][variant][slot].load(std::memory_order_relaxed);
-        if (per_cu <= 0) {
-            int nb = 0;
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, nt, 0);
-            if (e != hipSuccess) return e;
-            per_cu = nb > 0 ? nb : 1;
-            g_occ[dev][vpt - 1][variant][slot].store(per_cu, std::memory_order_relaxed);
-        }
-    }
-    const int64_t g = static_cast<int64_t>(cus) * per_cu;
-    *grid = T < g ? T : g;
-    return hipSuccess;
 }
 
 }  // namespace
@@ -354,7 +343,9 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     const uint64_t act = static_cast<uint64_t>(T) * H * 2;  // bytes of a [T, H] bf16 tensor
     const uint64_t meta = static_cast<uint64_t>(T) * K * 4;
     const uint64_t gam = static_cast<uint64_t>(H) * 2;
-    // residual_out may be exactly residual; any other overlap of an output is refused.
+    // residual_out may be exactly residual; any other overlap of an output is
+    // refused. expert_out's extent is unknown (R is not passed): only its first
+    // 16 bytes are checked.
     if (residual_out != residual && overlaps(residual_out, act, residual, act)) return MFR_ERR_ALIAS;
     if (overlaps(residual_out, act, shared_out, act) || overlaps(residual_out, act, gamma, gam) ||
         overlaps(residual_out, act, perm_idx, meta) || overlaps(residual_out, act, topk_w, meta) ||
@@ -384,18 +375,10 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     const int path = choose_path(T);
     const int vpt = choose_vpt(path, p.V);
     const int nt = threads_for(p.V, vpt);
-    const bool k8 = K == 8;
-    const void* kern = kernel_for(path, vpt, k8);
+    const void* kern = kernel_for(vpt, K == 8, write_through(path, T, H));
     void* args[] = {&p};
-    hipError_t e;
-    if (path == MFR_PATH_TOKEN) {
-        e = hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
-    } else {
-        int64_t grid = 0;
-        e = stream_grid(kern, vpt, k8 ? 1 : 0, nt, T, &grid);
-        if (e == hipSuccess)
-            e = hipLaunchKernel(kern, dim3(static_cast<uint32_t>(grid)), dim3(nt), args, 0, stream);
-    }
+    const hipError_t e =
+        hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
     return e == hipSuccess ? MFR_OK : MFR_ERR_HIP;
 }
 
@@ -418,13 +401,13 @@ const char* moe_finalize_rmsnorm_strerror(int status) {
     }
 }
 
-int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int wg_per_cu) {
+int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int store_policy) {
     if (path < 0 || path > MFR_PATH_STREAM) return MFR_ERR_ARG;
     if (vectors_per_thread < 0 || vectors_per_thread > kVptMax) return MFR_ERR_ARG;
-    if (wg_per_cu < 0 || wg_per_cu > 16) return MFR_ERR_ARG;
+    if (store_policy < 0 || store_policy > MFR_STORE_WRITE_THROUGH) return MFR_ERR_ARG;
     g_force_path.store(path, std::memory_order_relaxed);
     g_force_vpt.store(vectors_per_thread, std::memory_order_relaxed);
-    g_force_wgpcu.store(wg_per_cu, std::memory_order_relaxed);
+    g_force_store.store(store_policy, std::memory_order_relaxed);
     return MFR_OK;
 }
 
