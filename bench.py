@@ -16,7 +16,8 @@ T = 1..64 and the 512-token batch, plus a measured copy ceiling.
 Modes used with rocprofv3 (see profiles/):
   --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
                      size, for counter collection (FETCH_SIZE / WRITE_SIZE)
-  --summarize-stats  turn a rocprofv3 kernel_stats.csv into a profiles/ summary
+  --latency-run      eager calls at the decode sizes and the 512 batch, to trace
+  --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
 """
 import argparse
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused MoE-finalize+RMSNorm µs/call and effective HBM GB/s (% of peak), 1 MI355X"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FUSED_KERNEL_PREFIX = "mfr_"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stream_kernel_prefill_T8192.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_prefill_T8192_traffic.json")
 HEADLINE_CFG, HEADLINE_T = 4, 8192
 
 
@@ -105,20 +106,22 @@ def time_calls(calls, n, warmup):
     return e0.elapsed_time(e1) / n
 
 
-def time_graph(call, per_graph, replays):
-    """Mean device ms per call inside a captured graph of per_graph calls."""
+def time_graph(calls, per_call, replays):
+    """Mean device ms per call inside a captured graph that runs the list of
+    calls in turn, per_call times each (rotating buffer sets keep it cold)."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for _ in range(3):
-            call()
+        for c in calls:
+            c()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(per_graph):
-            call()
+        for _ in range(per_call):
+            for c in calls:
+                c()
     g.replay()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
@@ -128,7 +131,7 @@ def time_graph(call, per_graph, replays):
         g.replay()
     e1.record(st)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (per_graph * replays)
+    return e0.elapsed_time(e1) / (per_call * len(calls) * replays)
 
 
 def _probe_lib():
@@ -174,16 +177,19 @@ def probe_ceilings(nbytes=1 << 30, reps=10):
 # modes
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(d, passes=3):
-    """The oracle as it stands (single-threaded fp64 C++) on the same workload."""
+def cpu_baseline(d, min_seconds=10.0, max_passes=20):
+    """The oracle as it stands (single-threaded fp64 C++) on the same workload,
+    repeated whole until at least min_seconds of CPU work have been timed."""
     import oracle
     import synth
     nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     oracle.default()
     t0 = time.perf_counter()
-    for _ in range(passes):
+    passes = 0
+    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                                 d["residual"], d["gamma"], d["eps"], d["scale"], want_exact=False)
+        passes += 1
     dt = time.perf_counter() - t0
     cpu = "unknown"
     try:
@@ -211,33 +217,51 @@ def traffic_for_headline():
     return t.get("traffic_bytes_per_launch")
 
 
+DECODE_TS = (1, 4, 12, 28, 64)
+
+
 def decode_latency():
-    """Per-call device µs at the decode sizes (context figures)."""
+    """Per-call device µs at the decode sizes (H=6144, K=8), inside a graph of
+    100 back-to-back calls on one buffer set (the inputs stay in the Infinity
+    Cache, as right after GEMM2 wrote them). Context figures."""
     import synth
     out = {}
-    for T in synth.CONFIGS[1]["Ts"]:
+    for T in DECODE_TS:
         d = synth.config_inputs(1, T)
         dd = to_device(d)
         call, _ = make_caller(dd, d["eps"], d["scale"])
-        eager = time_calls([call], 200, 20) * 1e3
-        graph = time_graph(call, 100, 5) * 1e3
-        out[f"T{T}"] = {"graph_us": round(graph, 2), "stream_us": round(eager, 2)}
+        out[f"T{T}"] = round(time_graph([call], 100, 5) * 1e3, 2)
     return out
 
 
 def graph_ceiling_batch():
-    """The 512-token batch: cold (8 rotating buffer sets, 604 MB > Infinity
-    Cache) and warm (one set back to back)."""
+    """The 512-token batch (H=6144, K=8): HBM-cold (a graph cycling over 8
+    buffer sets, 604 MB > Infinity Cache) and cache-warm (one set)."""
     import synth
     d = synth.config_inputs(3, 512)
     nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     sets = [to_device(d) for _ in range(8)]
     calls = [make_caller(dd, d["eps"], d["scale"])[0] for dd in sets]
-    cold = time_calls(calls, 400, 16) * 1e3
-    warm = time_calls(calls[:1], 400, 16) * 1e3
+    cold = time_graph(calls, 8, 5) * 1e3
+    warm = time_graph(calls[:1], 64, 5) * 1e3
     return {"us_cold": round(cold, 2), "gbs_cold": round(nbytes / (cold * 1e-6) / 1e9, 1),
-            "us_warm": round(warm, 2), "gbs_warm": round(nbytes / (warm * 1e-6) / 1e9, 1),
-            "bytes": nbytes}
+            "frac_cold": round(nbytes / (cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "us_warm": round(warm, 2), "bytes": nbytes}
+
+
+def run_latency(args):
+    """Eager calls at the decode sizes and the 512 batch, for a kernel trace."""
+    import torch
+    import synth
+    torch.cuda.set_device(0)
+    for cfg, T in [(1, t) for t in DECODE_TS] + [(3, 512)]:
+        d = synth.config_inputs(cfg, T)
+        dd = to_device(d)
+        call, _ = make_caller(dd, d["eps"], d["scale"])
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        log(f"T={T}: {args.steps} calls")
 
 
 def run_bench(args):
@@ -287,7 +311,7 @@ def run_bench(args):
         log("measured ceilings (1 GiB copy and read probes)")
         cp, rd = probe_ceilings()
         rec["probe_ceilings_gbs"] = {"copy": round(cp, 1), "read_only": round(rd, 1)}
-        log("decode latency sweep T = 1..64 (H=6144, K=8)")
+        log("decode latency, T = 1..64 (H=6144, K=8), graph of 100 calls")
         rec["decode_latency_us"] = decode_latency()
         log("512-token batch, cold and warm")
         rec["batch_512"] = graph_ceiling_batch()
@@ -313,17 +337,25 @@ def run_pmc(args):
     log("pmc run done")
 
 
-def summarize_stats(args):
-    rows = list(csv.DictReader(open(args.summarize_stats)))
-    lines = [f"# rocprofv3 kernel statistics: {args.title}", "", "Command:", "",
+def summarize_trace(args):
+    """Per (kernel, grid, workgroup) durations from a rocprofv3 kernel_trace.csv."""
+    import statistics
+    groups = {}
+    for r in csv.DictReader(open(args.summarize_trace)):
+        name = r["Kernel_Name"]
+        if args.kernel_filter and args.kernel_filter not in name:
+            continue
+        key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# rocprofv3 kernel trace: {args.title}", "",
+             "Commands ($REPO is the repository root; the GPU run writes gpurun_out/):", "",
              "```", args.command, "```", "",
-             "| kernel | calls | avg µs | min µs | max µs | share % |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r.get("Name", "")
-        short = name if len(name) < 90 else name[:87] + "..."
-        lines.append(f"| `{short}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} | "
-                     f"{float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} | "
-                     f"{float(r.get('Percentage', 0)):.2f} |")
+             "| kernel | grid (threads) | workgroup | tokens | calls | avg µs | median µs | min µs | max µs |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        short = name.replace("(mfr::Params)", "")
+        lines.append(f"| `{short}` | {grid} | {wg} | {grid // wg} | {len(v)} | {statistics.mean(v):.2f} | "
+                     f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -348,8 +380,8 @@ def summarize_pmc(args):
         v = vals[ks[0]]
         return ks[0], sum(v) / len(v)
     copy_bytes = 1 << 30
-    fk, f_fused = pick(fetch, "mfr_stream_kernel")
-    _, w_fused = pick(write, "mfr_stream_kernel")
+    fk, f_fused = pick(fetch, "mfr_fused_kernel")
+    _, w_fused = pick(write, "mfr_fused_kernel")
     _, f_copy = pick(fetch, "mfr_copy_probe_kernel")
     _, w_copy = pick(write, "mfr_copy_probe_kernel")
     cf = copy_bytes / (f_copy * 1024.0)
@@ -377,7 +409,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip copy ceiling, decode sweep, 512 batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
-    ap.add_argument("--summarize-stats")
+    ap.add_argument("--latency-run", action="store_true")
+    ap.add_argument("--summarize-trace")
+    ap.add_argument("--kernel-filter", default="mfr_")
     ap.add_argument("--summarize-pmc", action="store_true")
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
@@ -385,8 +419,8 @@ def main():
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
     args = ap.parse_args()
-    if args.summarize_stats:
-        return summarize_stats(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -397,6 +431,8 @@ def main():
         sys.exit(2)
     if args.pmc_run:
         return run_pmc(args)
+    if args.latency_run:
+        return run_latency(args)
     return run_bench(args)
 
 
