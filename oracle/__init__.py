@@ -6,9 +6,11 @@ imports it and it never imports the GPU library; they share no code.
 
 The arithmetic lives in ``mfr_oracle.cpp`` (single-threaded C++17, fp64, one
 rounding to bf16 per output). This module only marshals numpy arrays into it.
-Source of the definition: vLLM pull request #62174 (deferred MoE finalize for
-GLM-5.x), sections Details and Validation; the header of ``mfr_oracle.cpp``
-lists the readings taken where the page is silent.
+Source of the definitions: vLLM pull request #62174 (deferred MoE finalize for
+GLM-5.x), sections Details and Validation, for finalize_rmsnorm; "Port the
+validated GLM-5.2 H200 production path to latest vLLM", Ported behavior, for
+the dense residual_rmsnorm. The header of ``mfr_oracle.cpp`` lists the readings
+taken where the pages are silent.
 
 Parity pins: every function here is pinned by tests/test_oracle.py (hand cases,
 closed forms, invariants, library special cases, exact brute force); none is
@@ -43,6 +45,8 @@ class Oracle:
             p, i64, p, p, p, p, p, ctypes.c_float, ctypes.c_float,
             i64, i64, i64, p, p, p, p,
         ]
+        lib.mfr_oracle_residual_rmsnorm.restype = ctypes.c_int
+        lib.mfr_oracle_residual_rmsnorm.argtypes = [p, p, p, ctypes.c_float, i64, i64, p, p, p, p]
         lib.mfr_oracle_rne_bf16_from_f64.restype = None
         lib.mfr_oracle_rne_bf16_from_f64.argtypes = [p, i64, p]
         self.path = path
@@ -97,6 +101,33 @@ class Oracle:
             out["normed_exact"] = ne
         return out
 
+    def residual_rmsnorm(self, x, residual, gamma, eps, want_exact=True):
+        """Dense residual add + RMSNorm (no routed part) on host arrays.
+
+        x, residual: uint16 [T, H] (bf16 bits); gamma: uint16 [H]; eps: fp32 value.
+        Same outputs as finalize_rmsnorm.
+        """
+        X = np.ascontiguousarray(x, dtype=np.uint16)
+        R = np.ascontiguousarray(residual, dtype=np.uint16)
+        G = np.ascontiguousarray(gamma, dtype=np.uint16)
+        if X.ndim != 2 or R.shape != X.shape or G.shape != (X.shape[1],):
+            raise ValueError("x and residual must be [T, H] and gamma [H]")
+        T, H = X.shape
+        res_out = np.empty((T, H), dtype=np.uint16)
+        nrm_out = np.empty((T, H), dtype=np.uint16)
+        s = np.empty((T, H), dtype=np.float64) if want_exact else None
+        ne = np.empty((T, H), dtype=np.float64) if want_exact else None
+        rc = self._lib.mfr_oracle_residual_rmsnorm(
+            _ptr(X), _ptr(R), _ptr(G), float(np.float32(eps)), T, H, _ptr(res_out), _ptr(nrm_out),
+            _ptr(s) if want_exact else None, _ptr(ne) if want_exact else None)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the shapes (status {rc})")
+        out = {"residual_out": res_out, "normed_out": nrm_out}
+        if want_exact:
+            out["s"] = s
+            out["normed_exact"] = ne
+        return out
+
     def rne_bf16_from_f64(self, x):
         """Round float64 values to bf16 bit patterns (ties to even), elementwise."""
         a = np.ascontiguousarray(x, dtype=np.float64)
@@ -120,6 +151,10 @@ def default():
 
 def finalize_rmsnorm(*args, **kwargs):
     return default().finalize_rmsnorm(*args, **kwargs)
+
+
+def residual_rmsnorm(*args, **kwargs):
+    return default().residual_rmsnorm(*args, **kwargs)
 
 
 def rne_bf16_from_f64(x):

@@ -158,6 +158,39 @@ int mfr_oracle_finalize_rmsnorm(const uint16_t* expert_out, int64_t R,
     return MFR_ORACLE_OK;
 }
 
+// Dense residual add + RMSNorm: the same tail with no routed part.
+// ("Port the validated GLM-5.2 H200 production path to latest vLLM", Ported
+// behavior: the attention and MLP row-parallel partial outputs are fused with
+// the all-reduce, the residual add and RMSNorm, and so are the final
+// main-model norm and the MTP final norm; on one GPU the all-reduce is the
+// identity.) Per token: s = x + residual in fp64, residual_out = RNE(s),
+// normed_out = RNE(s / sqrt(mean(s^2) + eps) * gamma).
+//   x, residual  [T, H] bf16 bits;  gamma [H] bf16 bits
+//   s_exact / normed_exact: optional unrounded outputs, as above.
+int mfr_oracle_residual_rmsnorm(const uint16_t* x, const uint16_t* residual,
+                                const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                uint16_t* residual_out, uint16_t* normed_out,
+                                double* s_exact, double* normed_exact) {
+    if (T < 0 || H <= 0) return MFR_ORACLE_ERR_SHAPE;
+    std::vector<double> s(static_cast<size_t>(H));
+    const double eps_d = static_cast<double>(eps);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h)
+            s[h] = bf16_bits_to_double(x[t * H + h]) + bf16_bits_to_double(residual[t * H + h]);
+        double sumsq = 0.0;
+        for (int64_t h = 0; h < H; ++h) sumsq += s[h] * s[h];
+        const double denom = std::sqrt(sumsq / static_cast<double>(H) + eps_d);
+        for (int64_t h = 0; h < H; ++h) {
+            const double y = s[h] / denom * bf16_bits_to_double(gamma[h]);
+            residual_out[t * H + h] = rne_bf16_from_f64(s[h]);
+            normed_out[t * H + h] = rne_bf16_from_f64(y);
+            if (s_exact) s_exact[t * H + h] = s[h];
+            if (normed_exact) normed_exact[t * H + h] = y;
+        }
+    }
+    return MFR_ORACLE_OK;
+}
+
 // Elementwise double -> bf16 rounding, exported so the rounding itself can be
 // pinned by the tests.
 void mfr_oracle_rne_bf16_from_f64(const double* x, int64_t n, uint16_t* out) {

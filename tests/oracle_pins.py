@@ -120,6 +120,11 @@ def hand_cases():
         return json.load(f)["cases"]
 
 
+def dense_hand_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["dense_cases"]
+
+
 def pin_hand_cases(o):
     for case in hand_cases():
         for eps in case["eps_values"]:
@@ -356,10 +361,77 @@ def pin_index_range(o):
     raise AssertionError("index == R was accepted")
 
 
+# --------------------------------------------------------------------------
+# Dense residual add + RMSNorm (no routed part)
+# --------------------------------------------------------------------------
+
+def pin_dense_hand_case(o):
+    for case in dense_hand_cases():
+        for eps in case["eps_values"]:
+            out = o.residual_rmsnorm(_bits(np.asarray(case["x"], dtype=np.float64)),
+                                     _bits(np.asarray(case["residual"], dtype=np.float64)),
+                                     _bits(np.asarray(case["gamma"], dtype=np.float64)), eps)
+            want_r = _bits(np.asarray(case["residual_out"], dtype=np.float64))
+            want_n = _bits(np.asarray(case["normed_out"], dtype=np.float64))
+            assert np.array_equal(out["residual_out"], want_r), (case["name"], eps)
+            assert np.array_equal(out["normed_out"], want_n), (case["name"], eps)
+
+
+def pin_dense_bruteforce_exact(o, n_cases=40, seed=77):
+    """Exact rationals on tiny dyadic inputs: s = x + residual rounded once,
+    the normed value from a 60-digit square root."""
+    rng = np.random.default_rng(seed)
+    for ci in range(n_cases):
+        T = int(rng.integers(1, 4))
+        H = int(rng.choice([8, 16]))
+        x = rng.integers(-32, 33, size=(T, H)) / 8.0
+        r = rng.integers(-64, 65, size=(T, H)) / 16.0
+        g = rng.integers(1, 17, size=H) / 8.0
+        eps = float(rng.choice([0.0, 2.0 ** -10, float(np.float32(1e-6))]))
+        out = o.residual_rmsnorm(_bits(x), _bits(r), _bits(g), eps)
+        for t in range(T):
+            s, normed = exact.exact_token([[0.0] * H], [-1], [0.0], x[t].tolist(), r[t].tolist(),
+                                          g.tolist(), eps, 1.0)
+            for h in range(H):
+                assert out["residual_out"][t, h] == exact.fraction_to_bf16_bits(s[h]), (ci, t, h)
+                if normed[h] is None:
+                    assert _is_nan_bits(out["normed_out"][t, h])
+                    continue
+                want = exact.fraction_to_bf16_bits(normed[h])
+                if out["normed_out"][t, h] != want:
+                    assert _near_tie(normed[h]), (ci, t, h, "normed")
+
+
+def pin_dense_rms_norm_library(o):
+    """torch.nn.functional.rms_norm in float64 of x + residual."""
+    d = synth.generate(16, 2048, 1, seed=12)
+    x, r = d["shared_out"], d["residual"]
+    out = o.residual_rmsnorm(x, r, d["gamma"], d["eps"])
+    s = exact.bf16_values(x) + exact.bf16_values(r)
+    assert np.array_equal(out["s"], s)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(s), (2048,),
+                                       weight=torch.from_numpy(exact.bf16_values(d["gamma"])),
+                                       eps=d["eps"]).numpy()
+    assert np.all(np.abs(out["normed_exact"] - ref) <= 1e-12 * np.abs(ref) + 1e-300)
+
+
+def pin_dense_equals_all_masked_finalize(o):
+    """The dense op on x equals the fused finalize with every slot masked and
+    shared = x (values equal; a zero may differ in sign only)."""
+    d = synth.generate(8, 1024, 4, scale=2.5, seed=13)
+    p = np.full_like(d["perm_idx"], -1)
+    a = o.finalize_rmsnorm(d["expert_out"], p, d["topk_w"], d["shared_out"], d["residual"],
+                           d["gamma"], d["eps"], d["scale"])
+    b = o.residual_rmsnorm(d["shared_out"], d["residual"], d["gamma"], d["eps"])
+    for k in ("residual_out", "normed_out"):
+        assert np.array_equal(exact.bf16_values(a[k]), exact.bf16_values(b[k])), k
+
+
 ALL_PINS = [
     pin_rne_roundtrip, pin_rne_midpoints, pin_rne_overflow_and_specials, pin_rne_vs_torch,
     pin_rne_vs_exact_random, pin_hand_cases, pin_bruteforce_exact, pin_sparse_matmul,
     pin_rms_norm_library, pin_closed_form_k1, pin_slot_permutation, pin_zero_routed,
     pin_scale_invariance, pin_unit_rms, pin_masked_nan_poison, pin_weight_zero_reads_row,
-    pin_index_range,
+    pin_index_range, pin_dense_hand_case, pin_dense_bruteforce_exact, pin_dense_rms_norm_library,
+    pin_dense_equals_all_masked_finalize,
 ]

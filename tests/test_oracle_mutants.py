@@ -30,6 +30,14 @@ MUTANTS = [
     ("ties_up", "r = (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "r = fl + 1.0;"),
     ("subnormals_flushed", "if (lead < -126) lead = -126;", "if (lead < -126) return sign;"),
     ("truncate_not_round", "if (frac > 0.5) {", "if (frac > 2.0) {"),
+    ("dense_drop_residual",
+     "bf16_bits_to_double(x[t * H + h]) + bf16_bits_to_double(residual[t * H + h]);",
+     "bf16_bits_to_double(x[t * H + h]);"),
+    ("dense_eps_outside_root", "std::sqrt(sumsq / static_cast<double>(H) + eps_d)",
+     "(std::sqrt(sumsq / static_cast<double>(H)) + eps_d)"),
+    ("dense_sum_not_mean", "sumsq / static_cast<double>(H) + eps_d", "sumsq + eps_d"),
+    ("dense_gamma_dropped", "const double y = s[h] / denom * bf16_bits_to_double(gamma[h]);\n            residual_out[t * H + h] = rne_bf16_from_f64(s[h]);\n            normed_out[t * H + h] = rne_bf16_from_f64(y);\n            if (s_exact) s_exact[t * H + h] = s[h];\n            if (normed_exact) normed_exact[t * H + h] = y;\n        }\n    }\n    return MFR_ORACLE_OK;\n}\n\n// Elementwise",
+     "const double y = s[h] / denom;\n            residual_out[t * H + h] = rne_bf16_from_f64(s[h]);\n            normed_out[t * H + h] = rne_bf16_from_f64(y);\n            if (s_exact) s_exact[t * H + h] = s[h];\n            if (normed_exact) normed_exact[t * H + h] = y;\n        }\n    }\n    return MFR_ORACLE_OK;\n}\n\n// Elementwise"),
 ]
 
 
