@@ -16,7 +16,8 @@ T = 1..64 and the 512-token batch, plus a measured copy ceiling.
 Modes used with rocprofv3 (see profiles/):
   --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
                      size, for counter collection (FETCH_SIZE / WRITE_SIZE)
-  --latency-run      eager calls at the decode sizes and the 512 batch, to trace
+  --latency-run      eager calls at the decode sizes and the 512 batch (and the
+                     dense op at T=28 and 8192), to trace
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
 """
@@ -249,6 +250,46 @@ def graph_ceiling_batch():
             "us_warm": round(warm, 2), "bytes": nbytes}
 
 
+def make_dense_caller(d):
+    """Zero-allocation closure for one dense residual add + RMSNorm call."""
+    import numpy as np
+    import torch
+    import top_finalize_residual_amd as mfr
+
+    def bf16(u):
+        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).cuda()
+    x, res, g = bf16(d["x"]), bf16(d["residual"]), bf16(d["gamma"])
+    ro, no = torch.empty_like(x), torch.empty_like(x)
+    T, H, eps = d["T"], d["H"], d["eps"]
+
+    def call():
+        rc = mfr.residual_add_rmsnorm_raw(x.data_ptr(), res.data_ptr(), g.data_ptr(), eps,
+                                          ro.data_ptr(), no.data_ptr(), T, H,
+                                          torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(mfr.strerror(rc))
+    call.keep = (x, res, g, ro, no)
+    return call
+
+
+def dense_figures():
+    """The dense residual add + RMSNorm (no routed part): the 8192-token chunk
+    HBM-cold (3 rotating buffer sets, 603 MB), and one decode step of 28 tokens
+    inside a graph."""
+    import synth
+    T, H = 8192, 6144
+    d = synth.dense_inputs(T, H, seed=synth.seed_for(4, T), spike_frac=0.01)
+    nbytes = synth.dense_algorithmic_bytes(T, H)
+    calls = [make_dense_caller(d) for _ in range(3)]
+    ms = time_calls(calls, 60, 6)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    small = synth.dense_inputs(28, H, seed=synth.seed_for(1, 28))
+    dec = time_graph([make_dense_caller(small)], 100, 5) * 1e3
+    return {"prefill_T8192": {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes},
+            "decode_T28_us": round(dec, 2)}
+
+
 def run_latency(args):
     """Eager calls at the decode sizes and the 512 batch, for a kernel trace."""
     import torch
@@ -262,6 +303,12 @@ def run_latency(args):
             call()
         torch.cuda.synchronize()
         log(f"T={T}: {args.steps} calls")
+    for T in (28, 8192):
+        call = make_dense_caller(synth.dense_inputs(T, 6144, seed=synth.seed_for(4, T)))
+        for _ in range(args.steps if T < 8192 else 20):
+            call()
+        torch.cuda.synchronize()
+        log(f"dense T={T}")
 
 
 def run_bench(args):
@@ -315,6 +362,8 @@ def run_bench(args):
         rec["decode_latency_us"] = decode_latency()
         log("512-token batch, cold and warm")
         rec["batch_512"] = graph_ceiling_batch()
+        log("dense residual add + RMSNorm (no routed part)")
+        rec["dense_residual_rmsnorm"] = dense_figures()
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on the same workload (single thread)")
         rec["cpu_baseline"] = cpu_baseline(d)

@@ -103,6 +103,26 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
                          uint16_t* residual_out, uint16_t* normed_out,
                          int64_t T, int64_t H, int64_t K, hipStream_t stream);
 
+/* Dense residual add + RMSNorm: the same tail with no routed part, for the
+ * layers whose row-parallel attention / MLP outputs, or the final main-model
+ * and MTP norms, feed the residual stream ("Port the validated GLM-5.2 H200
+ * production path to latest vLLM", Ported behavior: those outputs are fused
+ * with the all-reduce, the residual add and RMSNorm; on one GPU the all-reduce
+ * is the identity). For each token t and hidden index h:
+ *
+ *   s[h]              = x[t,h] + residual[t,h]            (fp32)
+ *   residual_out[t,h] = bf16(s[h])
+ *   normed_out[t,h]   = bf16(s[h] / sqrt(mean_h(s^2) + eps) * gamma[h])
+ *
+ *   x, residual, residual_out, normed_out  [T, H] bf16;  gamma [H] bf16.
+ * Limits, alignment (16 bytes for every pointer), ownership, stream ordering
+ * and errors as for moe_finalize_rmsnorm; residual_out may be exactly
+ * residual, and no other output may overlap an input or the other output.
+ * The launch shape follows the same rule of T as moe_finalize_rmsnorm_path. */
+int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                         float eps, uint16_t* residual_out, uint16_t* normed_out,
+                         int64_t T, int64_t H, hipStream_t stream);
+
 /* Which path moe_finalize_rmsnorm would take for this shape, taking any
  * override from moe_finalize_rmsnorm_force into account; MFR_PATH_UNSUPPORTED
  * if the shape is outside the limits. Pure host function: no HIP call. A

@@ -157,6 +157,20 @@ def generate(T, H, K, *, scale=2.5, eps=EPS, weights="softmax_k", mask_frac=0.0,
                 scale=float(np.float32(scale)), T=T, H=H, K=K, R=R, spike_rows=spike_rows)
 
 
+def dense_inputs(T, H, *, eps=EPS, seed=BASE_SEED, spike_frac=0.0):
+    """Inputs of the dense residual add + RMSNorm: x (a row-parallel layer
+    output, N(0, 0.5^2), drawn like shared_out) and residual (N(0, 4^2), with
+    the optional x100 rows) from the same streams as generate()."""
+    d = generate(T, H, 1, eps=eps, seed=seed, spike_frac=spike_frac)
+    return dict(x=d["shared_out"], residual=d["residual"], gamma=d["gamma"], eps=d["eps"], T=T,
+                H=H, spike_rows=d["spike_rows"])
+
+
+def dense_algorithmic_bytes(T, H):
+    """x, residual and both outputs (2H bytes each per token), plus gamma once."""
+    return 8 * H * T + 2 * H
+
+
 def config_inputs(cfg, T=None):
     """Inputs of a named workload config at token count T (default: its first T)."""
     c = CONFIGS[cfg]

@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
-                 "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force"):
+                 "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force",
+                 "residual_add_rmsnorm"):
         assert want in names
 
 
@@ -155,3 +156,29 @@ def test_aliasing_rules():
     assert call(normed_out=p["residual"]) == binding.MFR_ERR_ALIAS
     # in place (residual_out == residual) and touching buffers are accepted: the
     # GPU tests exercise them, since a call that passes validation launches
+
+
+def dense_call(T_=T, H_=H, eps=1e-6, **over):
+    act = T * H * 2
+    p = dict(x=A, residual=A + 4 * act, gamma=A + 8 * act, residual_out=A + 12 * act,
+             normed_out=A + 16 * act)
+    p.update(over)
+    return mfr.residual_add_rmsnorm_raw(p["x"], p["residual"], p["gamma"], eps, p["residual_out"],
+                                        p["normed_out"], T_, H_, None)
+
+
+def test_dense_validation():
+    act = T * H * 2
+    for name in ("x", "residual", "gamma", "residual_out", "normed_out"):
+        assert dense_call(**{name: None}) == binding.MFR_ERR_NULL, name
+        assert dense_call(**{name: A + 20 * act + 8}) == binding.MFR_ERR_ALIGN, name
+    for shape in ((-1, H), (T, 0), (T, 12), (T, 16392), (2**31, H)):
+        assert dense_call(*shape) == binding.MFR_ERR_SHAPE, shape
+    for eps in (-1.0, math.nan, math.inf):
+        assert dense_call(eps=eps) == binding.MFR_ERR_SCALAR
+    assert dense_call(normed_out=A + 12 * act) == binding.MFR_ERR_ALIAS  # == residual_out
+    assert dense_call(residual_out=A) == binding.MFR_ERR_ALIAS  # on x
+    assert dense_call(normed_out=A + 4 * act + 16) == binding.MFR_ERR_ALIAS  # inside residual
+    assert dense_call(residual_out=A + 4 * act + 16) == binding.MFR_ERR_ALIAS  # partial overlap
+    assert dense_call(residual_out=A + 8 * act) == binding.MFR_ERR_ALIAS  # on gamma
+    assert mfr.residual_add_rmsnorm_raw(None, None, None, 1e-6, None, None, 0, H, None) == binding.MFR_OK

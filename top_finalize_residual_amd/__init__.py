@@ -4,7 +4,8 @@ The op (vLLM pull request #62174, Details): for each token, the weighted sum
 of its K routed-expert GEMM2 rows gathered through a permutation map, times
 the routed scaling factor, plus the shared-expert output and the residual,
 rounded once to bf16 for the new residual stream, then RMSNorm with gamma and
-eps. Implemented by hand-written HIP kernels for gfx950 behind a C ABI
+eps. Also the same tail with no routed part (residual_add_rmsnorm). Both are
+hand-written HIP kernels for gfx950 behind a C ABI
 (include/moe_finalize_rmsnorm.h); this package is the thin Python binding.
 """
 from .binding import (  # noqa: F401
@@ -19,5 +20,7 @@ from .binding import (  # noqa: F401
     moe_finalize_rmsnorm_force,
     moe_finalize_rmsnorm_path,
     moe_finalize_rmsnorm_raw,
+    residual_add_rmsnorm,
+    residual_add_rmsnorm_raw,
     strerror,
 )

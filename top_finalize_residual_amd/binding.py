@@ -43,6 +43,8 @@ _lib.moe_finalize_rmsnorm_path.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_path.argtypes = [_i64, _i64, _i64]
 _lib.moe_finalize_rmsnorm_strerror.restype = ctypes.c_char_p
 _lib.moe_finalize_rmsnorm_strerror.argtypes = [ctypes.c_int]
+_lib.residual_add_rmsnorm.restype = ctypes.c_int
+_lib.residual_add_rmsnorm.argtypes = [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _p]
 _lib.moe_finalize_rmsnorm_force.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_force.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
 
@@ -132,6 +134,42 @@ def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gam
         expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
         residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale),
         residual_out.data_ptr(), normed_out.data_ptr(), T, H, K, stream.cuda_stream)
+    if rc != MFR_OK:
+        raise MFRError(rc)
+    return residual_out, normed_out
+
+
+def residual_add_rmsnorm_raw(x, residual, gamma, eps, residual_out, normed_out, T, H, stream):
+    """Direct C call with integer addresses; returns the status code."""
+    return _lib.residual_add_rmsnorm(x, residual, gamma, float(eps), residual_out, normed_out,
+                                     int(T), int(H), stream)
+
+
+def residual_add_rmsnorm(x, residual, gamma, eps, residual_out=None, normed_out=None, stream=None):
+    """Dense residual add + RMSNorm (no routed part) on the current (or given) stream.
+
+    x / residual [T, H] bf16, gamma [H] bf16. Outputs are allocated when not
+    given; residual_out may be `residual` itself. Returns (residual_out, normed_out).
+    """
+    _check(x, "x", torch.bfloat16, 2)
+    _check(residual, "residual", torch.bfloat16, 2)
+    _check(gamma, "gamma", torch.bfloat16, 1)
+    T, H = x.shape
+    if tuple(residual.shape) != (T, H) or gamma.shape[0] != H:
+        raise ValueError("x and residual must be [T, H] and gamma [H]")
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if normed_out is None:
+        normed_out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(residual_out, "residual_out", torch.bfloat16, 2)
+    _check(normed_out, "normed_out", torch.bfloat16, 2)
+    if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
+        raise ValueError("outputs must be [T, H]")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    rc = _lib.residual_add_rmsnorm(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
+                                   residual_out.data_ptr(), normed_out.data_ptr(), T, H,
+                                   stream.cuda_stream)
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_out

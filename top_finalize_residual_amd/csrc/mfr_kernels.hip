@@ -119,7 +119,8 @@ __device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&id
 
 // One token, end to end. KT: 8 = exactly eight slots (the GLM-5.x / DeepSeek
 // top-8 case, no slot-count checks); 0 = any K in 1..16, as one or two
-// chunks of eight. Thread i owns the byte offsets 16*(i + j*NT), j < VPT, of
+// chunks of eight; -1 = no routed part (the dense residual add + RMSNorm:
+// shared_out holds x and s = x + residual). Thread i owns the byte offsets 16*(i + j*NT), j < VPT, of
 // every row; offsets at or past the row end (a ragged last tile) fall outside
 // the descriptors' range, so their loads return zero and their stores are
 // dropped by the hardware.
@@ -139,12 +140,13 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     // that waits for the metadata. The scheduling barrier keeps the compiler
     // from sinking those independent loads below the metadata wait, so every
     // workgroup starts streaming HBM one memory latency earlier.
+    constexpr bool DENSE = KT < 0;
     constexpr bool CHECK_K = KT != 8;
     const int32_t* prow = p.perm_idx + t * p.K;
     const float* wrow = p.topk_w + t * p.K;
     int32_t idx[8];
     float wr[8];
-    load_meta8<CHECK_K>(p, prow, wrow, 0, idx, wr);
+    if constexpr (!DENSE) load_meta8<CHECK_K>(p, prow, wrow, 0, idx, wr);
 
     const rsrc_t sh_r = make_rsrc(p.shared_out + trow, rowbytes);
     const rsrc_t rs_r = make_rsrc(p.residual + trow, rowbytes);
@@ -164,20 +166,26 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
 
-    gather_rows8<VPT, CHECK_K>(p, idx, wr, 0, off, acc);
-    if (CHECK_K && p.K > 8) {
-        load_meta8<true>(p, prow, wrow, 8, idx, wr);
-        gather_rows8<VPT, true>(p, idx, wr, 8, off, acc);
+    if constexpr (!DENSE) {
+        gather_rows8<VPT, CHECK_K>(p, idx, wr, 0, off, acc);
+        if (CHECK_K && p.K > 8) {
+            load_meta8<true>(p, prow, wrow, 8, idx, wr);
+            gather_rows8<VPT, true>(p, idx, wr, 8, off, acc);
+        }
     }
 
-    // s = (routed + shared) + residual; residual_out = bf16(s); per-lane sum of squares.
+    // s = (routed + shared) + residual (dense: x + residual); residual_out =
+    // bf16(s); per-lane sum of squares.
     const rsrc_t ro_r = make_rsrc(p.residual_out + trow, rowbytes);
     float ss = 0.0f;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            acc[j][e] = (acc[j][e] + vec_elem(sh[j], e)) + vec_elem(rs[j], e);
+            if constexpr (DENSE)
+                acc[j][e] = vec_elem(sh[j], e) + vec_elem(rs[j], e);
+            else
+                acc[j][e] = (acc[j][e] + vec_elem(sh[j], e)) + vec_elem(rs[j], e);
             ss = __builtin_fmaf(acc[j][e], acc[j][e], ss);
         }
         u32x4 o;
@@ -304,19 +312,61 @@ const void* pick_store(bool wt) {
               : reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut>);
 }
 
+// Routing variant of a launch: exactly eight slots, any K, or no routed part.
+enum Variant { kTop8 = 8, kAnyK = 0, kDense = -1 };
+
 template <int VPT>
-const void* pick(bool k8, bool wt) {
-    return k8 ? pick_store<VPT, 8>(wt) : pick_store<VPT, 0>(wt);
+const void* pick(Variant v, bool wt) {
+    switch (v) {
+        case kTop8: return pick_store<VPT, 8>(wt);
+        case kAnyK: return pick_store<VPT, 0>(wt);
+        default: return pick_store<VPT, -1>(wt);
+    }
 }
 
-// Kernel address for (vectors per thread, K == 8, write-through outputs).
-const void* kernel_for(int vpt, bool k8, bool wt) {
+// Kernel address for (vectors per thread, routing variant, write-through outputs).
+const void* kernel_for(int vpt, Variant v, bool wt) {
     switch (vpt) {
-        case 1: return pick<1>(k8, wt);
-        case 2: return pick<2>(k8, wt);
-        case 3: return pick<3>(k8, wt);
-        default: return pick<4>(k8, wt);
+        case 1: return pick<1>(v, wt);
+        case 2: return pick<2>(v, wt);
+        case 3: return pick<3>(v, wt);
+        default: return pick<4>(v, wt);
     }
+}
+
+// Output checks shared by both entry points: residual_out may be exactly
+// residual; otherwise neither output may overlap an input or the other output.
+// `others` are the remaining inputs with their byte extents.
+struct Extent {
+    const void* p;
+    uint64_t n;
+};
+
+int check_outputs(const void* residual_out, const void* normed_out, const void* residual,
+                  uint64_t act, const Extent* others, int n_others) {
+    if (residual_out != residual && overlaps(residual_out, act, residual, act)) return MFR_ERR_ALIAS;
+    if (overlaps(residual_out, act, normed_out, act) || overlaps(normed_out, act, residual, act))
+        return MFR_ERR_ALIAS;
+    for (int i = 0; i < n_others; ++i)
+        if (overlaps(residual_out, act, others[i].p, others[i].n) ||
+            overlaps(normed_out, act, others[i].p, others[i].n))
+            return MFR_ERR_ALIAS;
+    return MFR_OK;
+}
+
+// Fills the shape fields, picks the launch shape and enqueues the kernel.
+int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, hipStream_t stream) {
+    p.T = T;
+    p.h_f = static_cast<float>(H);
+    p.V = static_cast<int>(H / 8);
+    const int path = choose_path(T);
+    const int vpt = choose_vpt(path, p.V);
+    const int nt = threads_for(p.V, vpt);
+    const void* kern = kernel_for(vpt, v, write_through(path, T, H));
+    void* args[] = {&p};
+    const hipError_t e =
+        hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
+    return e == hipSuccess ? MFR_OK : MFR_ERR_HIP;
 }
 
 }  // namespace
@@ -342,19 +392,12 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
 
     const uint64_t act = static_cast<uint64_t>(T) * H * 2;  // bytes of a [T, H] bf16 tensor
     const uint64_t meta = static_cast<uint64_t>(T) * K * 4;
-    const uint64_t gam = static_cast<uint64_t>(H) * 2;
-    // residual_out may be exactly residual; any other overlap of an output is
-    // refused. expert_out's extent is unknown (R is not passed): only its first
-    // 16 bytes are checked.
-    if (residual_out != residual && overlaps(residual_out, act, residual, act)) return MFR_ERR_ALIAS;
-    if (overlaps(residual_out, act, shared_out, act) || overlaps(residual_out, act, gamma, gam) ||
-        overlaps(residual_out, act, perm_idx, meta) || overlaps(residual_out, act, topk_w, meta) ||
-        overlaps(residual_out, act, normed_out, act) || overlaps(residual_out, act, expert_out, 16))
-        return MFR_ERR_ALIAS;
-    if (overlaps(normed_out, act, residual, act) || overlaps(normed_out, act, shared_out, act) ||
-        overlaps(normed_out, act, gamma, gam) || overlaps(normed_out, act, perm_idx, meta) ||
-        overlaps(normed_out, act, topk_w, meta) || overlaps(normed_out, act, expert_out, 16))
-        return MFR_ERR_ALIAS;
+    // expert_out's extent is unknown (R is not passed): only its first 16
+    // bytes are checked.
+    const Extent others[] = {{shared_out, act}, {gamma, static_cast<uint64_t>(H) * 2},
+                             {perm_idx, meta}, {topk_w, meta}, {expert_out, 16}};
+    const int rc = check_outputs(residual_out, normed_out, residual, act, others, 5);
+    if (rc != MFR_OK) return rc;
 
     mfr::Params p;
     p.expert_out = reinterpret_cast<const mfr::u32x4*>(expert_out);
@@ -365,21 +408,37 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     p.gamma = reinterpret_cast<const mfr::u32x4*>(gamma);
     p.residual_out = reinterpret_cast<mfr::u32x4*>(residual_out);
     p.normed_out = reinterpret_cast<mfr::u32x4*>(normed_out);
-    p.T = T;
     p.eps = eps;
     p.scale = scale;
-    p.h_f = static_cast<float>(H);
-    p.V = static_cast<int>(H / 8);
     p.K = static_cast<int>(K);
+    return launch(p, T, H, K == 8 ? kTop8 : kAnyK, stream);
+}
 
-    const int path = choose_path(T);
-    const int vpt = choose_vpt(path, p.V);
-    const int nt = threads_for(p.V, vpt);
-    const void* kern = kernel_for(vpt, K == 8, write_through(path, T, H));
-    void* args[] = {&p};
-    const hipError_t e =
-        hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
-    return e == hipSuccess ? MFR_OK : MFR_ERR_HIP;
+int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                         float eps, uint16_t* residual_out, uint16_t* normed_out, int64_t T,
+                         int64_t H, hipStream_t stream) {
+    if (!shape_ok(T, H, 1)) return MFR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return MFR_ERR_SCALAR;
+    if (T == 0) return MFR_OK;
+    if (!x || !residual || !gamma || !residual_out || !normed_out) return MFR_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gamma, 16) ||
+        !aligned(residual_out, 16) || !aligned(normed_out, 16))
+        return MFR_ERR_ALIGN;
+    const uint64_t act = static_cast<uint64_t>(T) * H * 2;
+    const Extent others[] = {{x, act}, {gamma, static_cast<uint64_t>(H) * 2}};
+    const int rc = check_outputs(residual_out, normed_out, residual, act, others, 2);
+    if (rc != MFR_OK) return rc;
+
+    mfr::Params p = {};
+    p.shared_out = reinterpret_cast<const mfr::u32x4*>(x);
+    p.residual = reinterpret_cast<const mfr::u32x4*>(residual);
+    p.gamma = reinterpret_cast<const mfr::u32x4*>(gamma);
+    p.residual_out = reinterpret_cast<mfr::u32x4*>(residual_out);
+    p.normed_out = reinterpret_cast<mfr::u32x4*>(normed_out);
+    p.eps = eps;
+    p.scale = 1.0f;
+    p.K = 0;
+    return launch(p, T, H, kDense, stream);
 }
 
 int moe_finalize_rmsnorm_path(int64_t T, int64_t H, int64_t K) {
