@@ -290,6 +290,28 @@ def dense_figures():
             "decode_T28_us": round(dec, 2)}
 
 
+def deferred_overhead():
+    """Host cost of the torch-facing deferred path at one decode step (T=28):
+    eager calls through fused_add_rmsnorm (custom op dispatch + ctypes) and
+    through the raw C call, against the same call replayed from a graph."""
+    import torch
+    import synth
+    import top_finalize_residual_amd as mfr
+    d = synth.config_inputs(1, 28)
+    dd = to_device(d)
+    u = mfr.UnfinalizedMoEOutput(dd["expert_out"], dd["perm_idx"], dd["topk_w"], d["scale"])
+    mo = mfr.MoEOutput(u, dd["shared_out"])
+    ro, no = torch.empty_like(dd["residual"]), torch.empty_like(dd["residual"])
+
+    def via_op():
+        mfr.fused_add_rmsnorm(mo, dd["residual"], dd["gamma"], d["eps"], residual_out=ro,
+                              normed_out=no)
+    raw, _ = make_caller(dd, d["eps"], d["scale"])
+    return {"T": 28, "eager_op_us": round(time_calls([via_op], 300, 30) * 1e3, 2),
+            "eager_raw_us": round(time_calls([raw], 300, 30) * 1e3, 2),
+            "graph_op_us": round(time_graph([via_op], 100, 5) * 1e3, 2)}
+
+
 def run_latency(args):
     """Eager calls at the decode sizes and the 512 batch, for a kernel trace."""
     import torch
@@ -364,6 +386,8 @@ def run_bench(args):
         rec["batch_512"] = graph_ceiling_batch()
         log("dense residual add + RMSNorm (no routed part)")
         rec["dense_residual_rmsnorm"] = dense_figures()
+        log("deferred-finalize torch path: host overhead")
+        rec["deferred_path"] = deferred_overhead()
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on the same workload (single thread)")
         rec["cpu_baseline"] = cpu_baseline(d)

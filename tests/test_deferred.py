@@ -1,0 +1,51 @@
+"""The deferred-finalize contract on the host: the producer's deferral check,
+the MoEOutput containers and the torch custom-op registration (fake tensors,
+no GPU)."""
+import pytest
+import torch
+
+mfr = pytest.importorskip("top_finalize_residual_amd", reason="HIP library not built")
+
+
+def test_defer_check_follows_the_kernel_limits():
+    assert mfr.defer_moe_finalize(4, 6144, 8)
+    assert mfr.defer_moe_finalize(8192, 6144, 8)
+    assert mfr.defer_moe_finalize(1, 2048, 1)
+    assert not mfr.defer_moe_finalize(4, 6143, 8)   # H not a multiple of 8
+    assert not mfr.defer_moe_finalize(4, 32768, 8)  # H above 16384
+    assert not mfr.defer_moe_finalize(4, 6144, 17)  # K above 16
+    assert not mfr.defer_moe_finalize(-1, 6144, 8)
+
+
+def test_moe_output_containers():
+    E = torch.empty(32, 64, dtype=torch.bfloat16)
+    p = torch.zeros(4, 8, dtype=torch.int32)
+    w = torch.zeros(4, 8)
+    u = mfr.UnfinalizedMoEOutput(E, p, w, scale=2.5)
+    assert (u.num_tokens, u.hidden_size, u.top_k) == (4, 64, 8)
+    assert mfr.MoEOutput(u, torch.empty(4, 64, dtype=torch.bfloat16)).deferred
+    assert not mfr.MoEOutput(torch.empty(4, 64, dtype=torch.bfloat16),
+                             torch.empty(4, 64, dtype=torch.bfloat16)).deferred
+
+
+def test_custom_ops_are_registered_with_fake_kernels():
+    from torch._subclasses.fake_tensor import FakeTensorMode
+    assert hasattr(torch.ops.mfr, "moe_finalize_rmsnorm")
+    assert hasattr(torch.ops.mfr, "residual_add_rmsnorm")
+    with FakeTensorMode():
+        x = torch.empty(4, 64, dtype=torch.bfloat16)
+        r, n = mfr.fused_add_rmsnorm(x, torch.empty_like(x), torch.empty(64, dtype=torch.bfloat16),
+                                     1e-6)
+        assert r.shape == (4, 64) and n.shape == (4, 64)
+        u = mfr.UnfinalizedMoEOutput(torch.empty(32, 64, dtype=torch.bfloat16),
+                                     torch.zeros(4, 8, dtype=torch.int32), torch.zeros(4, 8))
+        r, n = mfr.fused_add_rmsnorm(mfr.MoEOutput(u, x), x, torch.empty(64, dtype=torch.bfloat16),
+                                     1e-6, in_place=True)
+        assert r is x
+
+
+def test_cpu_tensors_are_refused():
+    # the product path has no CPU fallback
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        mfr.fused_add_rmsnorm(x, torch.zeros_like(x), torch.ones(64, dtype=torch.bfloat16), 1e-6)

@@ -1,0 +1,110 @@
+"""GPU checks of the deferred-finalize contract: the consumer norm dispatches
+to the right kernel, bit-identical to the direct calls, and a captured graph of
+a decoder tail replays correctly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_finalize_residual_amd as mfr
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(d):
+    dd = gu.to_device(d)
+    return dd, mfr.UnfinalizedMoEOutput(dd["expert_out"], dd["perm_idx"], dd["topk_w"], d["scale"])
+
+
+@pytest.mark.parametrize("T", [4, 28, 512])
+def test_deferred_moe_output_equals_direct_call(T):
+    d = synth.generate(T, 6144, 8, scale=2.5, mask_frac=0.05, seed=600 + T)
+    dd, u = _dev(d)
+    assert mfr.defer_moe_finalize(T, 6144, 8)
+    r, n = mfr.fused_add_rmsnorm(mfr.MoEOutput(u, dd["shared_out"]), dd["residual"], dd["gamma"],
+                                 d["eps"])
+    torch.cuda.synchronize()
+    r0, n0 = gu.run(dd, d["eps"], d["scale"])
+    assert np.array_equal(gu.host_u16(r), r0) and np.array_equal(gu.host_u16(n), n0)
+
+
+def test_finalized_routed_part_goes_through_the_fused_kernel():
+    """A MoEOutput whose routed part is already a [T, H] tensor: routed +
+    shared + residual with one rounding, then RMSNorm (checked against the
+    oracle with K = 1, identity map, weight 1)."""
+    d = synth.generate(64, 2048, 1, scale=1.0, seed=61)
+    routed = d["expert_out"][d["perm_idx"][:, 0]]  # one [T, H] routed tensor
+    dd = gu.to_device(d)
+    r, n = mfr.fused_add_rmsnorm(mfr.MoEOutput(gu.dev_bf16(routed), dd["shared_out"]),
+                                 dd["residual"], dd["gamma"], d["eps"])
+    torch.cuda.synchronize()
+    ident = np.arange(64, dtype=np.int32)[:, None]
+    ref = oracle.finalize_rmsnorm(routed, ident, np.ones((64, 1), np.float32), d["shared_out"],
+                                  d["residual"], d["gamma"], d["eps"], 1.0)
+    gu.check(d, gu.host_u16(r), gu.host_u16(n), ref=ref)
+
+
+def test_plain_tensor_goes_to_the_dense_kernel_in_place():
+    d = synth.dense_inputs(28, 6144, seed=62)
+    x, res, g = gu.dev_bf16(d["x"]), gu.dev_bf16(d["residual"]), gu.dev_bf16(d["gamma"])
+    r0, n0 = mfr.residual_add_rmsnorm(x, res, g, d["eps"])
+    r, n = mfr.fused_add_rmsnorm(x, res, g, d["eps"], in_place=True)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == res.data_ptr()
+    assert np.array_equal(gu.host_u16(r), gu.host_u16(r0))
+    assert np.array_equal(gu.host_u16(n), gu.host_u16(n0))
+
+
+def test_custom_ops_pass_opcheck():
+    d = synth.generate(4, 2048, 8, seed=63)
+    dd = gu.to_device(d)
+    ro, no = torch.empty_like(dd["residual"]), torch.empty_like(dd["residual"])
+    torch.library.opcheck(torch.ops.mfr.moe_finalize_rmsnorm.default,
+                          (dd["expert_out"], dd["perm_idx"], dd["topk_w"], dd["shared_out"],
+                           dd["residual"], dd["gamma"], d["eps"], d["scale"], ro, no),
+                          test_utils=("test_schema", "test_faketensor"))
+    torch.library.opcheck(torch.ops.mfr.residual_add_rmsnorm.default,
+                          (dd["shared_out"], dd["residual"], dd["gamma"], d["eps"], ro, no),
+                          test_utils=("test_schema", "test_faketensor"))
+
+
+def test_decoder_tail_graph_replay():
+    """Two layer boundaries of a decode step: a dense (attention) output into
+    the post-attention norm, then the MoE layer's deferred output into the next
+    layer's input norm; captured once, replayed many times."""
+    T, H, K = 28, 6144, 8
+    d = synth.generate(T, H, K, scale=2.5, seed=64)
+    dd, u = _dev(d)
+    attn_out = gu.dev_bf16(synth.dense_inputs(T, H, seed=65)["x"])
+    res0 = dd["residual"].clone()
+    g1, g2 = dd["gamma"], gu.dev_bf16(synth.dense_inputs(T, H, seed=66)["gamma"])
+
+    def step(res):
+        res, h = mfr.fused_add_rmsnorm(attn_out, res, g1, d["eps"], in_place=True)
+        res, h2 = mfr.fused_add_rmsnorm(mfr.MoEOutput(u, dd["shared_out"]), res, g2, d["eps"],
+                                        in_place=True, normed_out=h)
+        return res, h2
+
+    res_e = res0.clone()
+    _, h_e = step(res_e)
+    torch.cuda.synchronize()
+    want_res, want_h = gu.host_u16(res_e), gu.host_u16(h_e)
+
+    res_g = res0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(res_g.clone())
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _, h_g = step(res_g)
+    for i in range(10):
+        res_g.copy_(res0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.host_u16(res_g), want_res), i
+        assert np.array_equal(gu.host_u16(h_g), want_h), i

@@ -24,3 +24,9 @@ from .binding import (  # noqa: F401
     residual_add_rmsnorm_raw,
     strerror,
 )
+from .deferred import (  # noqa: F401,E402
+    MoEOutput,
+    UnfinalizedMoEOutput,
+    defer_moe_finalize,
+    fused_add_rmsnorm,
+)

@@ -1,0 +1,150 @@
+"""Deferred MoE finalize for torch callers: the caller side of the fused op.
+
+The contract (vLLM pull request #62174, Overview and Details): a decode MoE
+layer may leave its top-k reduction open and hand the next layer a MoEOutput
+that holds the unfinalized routed part (the GEMM2 rows, the permutation map
+and the routing weights) plus the shared-expert output. The next layer's input
+norm then finalizes it, adds the residual and normalises in one kernel. A layer
+defers only when the fused kernel will run for the shape; otherwise it
+finalizes as before. The consumer owns and frees the deferred buffers once the
+fused kernel has been enqueued.
+
+Here:
+  * ``UnfinalizedMoEOutput`` / ``MoEOutput`` carry the deferred tensors;
+  * ``defer_moe_finalize(T, H, K)`` is the producer's check (the library's
+    path query, a host function: no GPU work, safe during graph capture);
+  * ``fused_add_rmsnorm(hidden, residual, gamma, eps)`` is the consumer norm:
+    a deferred MoEOutput goes to the fused finalize kernel, a plain tensor
+    (attention / dense MLP output) to the dense residual add + RMSNorm kernel;
+  * both kernels are registered as torch custom ops (``mfr::moe_finalize_rmsnorm``
+    and ``mfr::residual_add_rmsnorm``) that write into caller-provided outputs, so
+    torch sees their effects and CUDA/HIP graph capture records them.
+Every step of the arithmetic runs in the HIP library; nothing here computes.
+"""
+from dataclasses import dataclass
+from typing import Optional, Tuple, Union
+
+import torch
+
+from . import binding
+
+_LIB_NS = "mfr"
+
+
+@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm",
+                         mutates_args=("residual_out", "normed_out"))
+def _moe_finalize_rmsnorm_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
+                             topk_w: torch.Tensor, shared_out: torch.Tensor,
+                             residual: torch.Tensor, gamma: torch.Tensor, eps: float, scale: float,
+                             residual_out: torch.Tensor, normed_out: torch.Tensor) -> None:
+    binding.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
+                                 scale, residual_out=residual_out, normed_out=normed_out)
+
+
+@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm",
+                         mutates_args=("residual_out", "normed_out"))
+def _residual_add_rmsnorm_op(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                             eps: float, residual_out: torch.Tensor,
+                             normed_out: torch.Tensor) -> None:
+    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual_out,
+                                 normed_out=normed_out)
+
+
+@_moe_finalize_rmsnorm_op.register_fake
+def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
+      normed_out):
+    return None
+
+
+@_residual_add_rmsnorm_op.register_fake
+def _(x, residual, gamma, eps, residual_out, normed_out):
+    return None
+
+
+@dataclass
+class UnfinalizedMoEOutput:
+    """The routed part of a MoE layer whose top-k reduction is still open.
+
+    expert_out: [R, H] bf16 GEMM2 output rows; perm_idx: [T, K] int32 row of
+    each (token, slot), negative = masked; topk_w: [T, K] fp32 routing weights;
+    scale: routed scaling factor (1.0 when the router folded it into topk_w).
+    """
+    expert_out: torch.Tensor
+    perm_idx: torch.Tensor
+    topk_w: torch.Tensor
+    scale: float = 1.0
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.perm_idx.shape[0])
+
+    @property
+    def hidden_size(self) -> int:
+        return int(self.expert_out.shape[1])
+
+    @property
+    def top_k(self) -> int:
+        return int(self.perm_idx.shape[1])
+
+
+@dataclass
+class MoEOutput:
+    """A MoE layer's output handed to the next layer's norm: the routed part
+    (deferred, or already a [T, H] tensor) and the shared-expert output."""
+    routed: Union[UnfinalizedMoEOutput, torch.Tensor]
+    shared: torch.Tensor
+
+    @property
+    def deferred(self) -> bool:
+        return isinstance(self.routed, UnfinalizedMoEOutput)
+
+
+def defer_moe_finalize(num_tokens: int, hidden_size: int, top_k: int) -> bool:
+    """True if the fused finalize accepts this shape, so a producer may leave
+    its top-k reduction open. Host-only; no GPU work."""
+    return binding.moe_finalize_rmsnorm_path(num_tokens, hidden_size, top_k) != binding.PATH_UNSUPPORTED
+
+
+def _outputs(ref: torch.Tensor, residual: torch.Tensor, residual_out, normed_out, in_place):
+    if residual_out is None:
+        residual_out = residual if in_place else torch.empty_like(ref)
+    if normed_out is None:
+        normed_out = torch.empty_like(ref)
+    return residual_out, normed_out
+
+
+def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Tensor,
+                      gamma: torch.Tensor, eps: float, *, in_place: bool = False,
+                      residual_out: Optional[torch.Tensor] = None,
+                      normed_out: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The consumer norm of the next layer.
+
+    hidden: a MoEOutput (deferred or finalized routed part plus shared output)
+    or a plain [T, H] bf16 tensor (a dense layer's output).
+    Returns (new residual stream, normed hidden state), both [T, H] bf16.
+    in_place: write the new residual stream into `residual` itself.
+    """
+    if isinstance(hidden, MoEOutput):
+        shared = hidden.shared
+        residual_out, normed_out = _outputs(shared, residual, residual_out, normed_out, in_place)
+        if hidden.deferred:
+            r = hidden.routed
+            torch.ops.mfr.moe_finalize_rmsnorm(r.expert_out, r.perm_idx, r.topk_w, shared,
+                                               residual, gamma, float(eps), float(r.scale),
+                                               residual_out, normed_out)
+        else:
+            # An already finalized routed part goes through the same kernel as
+            # a single routed row per token (weight 1, scale 1), which keeps
+            # the one-rounding contract for routed + shared + residual.
+            routed = hidden.routed
+            T = routed.shape[0]
+            ident = torch.arange(T, dtype=torch.int32, device=routed.device).unsqueeze(1)
+            ones = torch.ones((T, 1), dtype=torch.float32, device=routed.device)
+            torch.ops.mfr.moe_finalize_rmsnorm(routed, ident, ones, shared, residual, gamma,
+                                               float(eps), 1.0, residual_out, normed_out)
+        return residual_out, normed_out
+    residual_out, normed_out = _outputs(hidden, residual, residual_out, normed_out, in_place)
+    torch.ops.mfr.residual_add_rmsnorm(hidden, residual, gamma, float(eps), residual_out,
+                                       normed_out)
+    return residual_out, normed_out
