@@ -9,7 +9,8 @@ rounding to bf16 per output). This module only marshals numpy arrays into it.
 Source of the definitions: vLLM pull request #62174 (deferred MoE finalize for
 GLM-5.x), sections Details and Validation, for finalize_rmsnorm; "Port the
 validated GLM-5.2 H200 production path to latest vLLM", Ported behavior, for
-the dense residual_rmsnorm. The header of ``mfr_oracle.cpp`` lists the readings
+the dense residual_rmsnorm, and Prepared experiment branches (dynamic
+per-token FP8 activations) for fp8_quantize_rows. The header of ``mfr_oracle.cpp`` lists the readings
 taken where the pages are silent.
 
 Parity pins: every function here is pinned by tests/test_oracle.py (hand cases,
@@ -47,6 +48,10 @@ class Oracle:
         ]
         lib.mfr_oracle_residual_rmsnorm.restype = ctypes.c_int
         lib.mfr_oracle_residual_rmsnorm.argtypes = [p, p, p, ctypes.c_float, i64, i64, p, p, p, p]
+        lib.mfr_oracle_fp8_quantize_rows.restype = None
+        lib.mfr_oracle_fp8_quantize_rows.argtypes = [p, i64, i64, p, p, p]
+        lib.mfr_oracle_rne_e4m3_from_f64.restype = None
+        lib.mfr_oracle_rne_e4m3_from_f64.argtypes = [p, i64, p]
         lib.mfr_oracle_rne_bf16_from_f64.restype = None
         lib.mfr_oracle_rne_bf16_from_f64.argtypes = [p, i64, p]
         self.path = path
@@ -128,6 +133,29 @@ class Oracle:
             out["normed_exact"] = ne
         return out
 
+    def fp8_quantize_rows(self, y):
+        """Dynamic per-row E4M3 quantisation of float64 rows [T, H].
+
+        Returns (codes uint8 [T, H], scales float64 [T], scaled float64 [T, H]),
+        where scaled = y / scale before rounding.
+        """
+        Y = np.ascontiguousarray(y, dtype=np.float64)
+        if Y.ndim != 2:
+            raise ValueError("y must be [T, H]")
+        T, H = Y.shape
+        codes = np.empty((T, H), dtype=np.uint8)
+        scales = np.empty(T, dtype=np.float64)
+        scaled = np.empty((T, H), dtype=np.float64)
+        self._lib.mfr_oracle_fp8_quantize_rows(_ptr(Y), T, H, _ptr(codes), _ptr(scales), _ptr(scaled))
+        return codes, scales, scaled
+
+    def rne_e4m3_from_f64(self, x):
+        """Round float64 values to E4M3 codes (ties to even, saturating at 448)."""
+        a = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint8)
+        self._lib.mfr_oracle_rne_e4m3_from_f64(_ptr(a), a.size, _ptr(out))
+        return out
+
     def rne_bf16_from_f64(self, x):
         """Round float64 values to bf16 bit patterns (ties to even), elementwise."""
         a = np.ascontiguousarray(x, dtype=np.float64)
@@ -155,6 +183,14 @@ def finalize_rmsnorm(*args, **kwargs):
 
 def residual_rmsnorm(*args, **kwargs):
     return default().residual_rmsnorm(*args, **kwargs)
+
+
+def fp8_quantize_rows(y):
+    return default().fp8_quantize_rows(y)
+
+
+def rne_e4m3_from_f64(x):
+    return default().rne_e4m3_from_f64(x)
 
 
 def rne_bf16_from_f64(x):

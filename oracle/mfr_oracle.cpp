@@ -90,6 +90,44 @@ uint16_t rne_bf16_from_f64(double x) {
     return static_cast<uint16_t>(sign | static_cast<uint16_t>(u >> 16));
 }
 
+// Round a double to OCP FP8 E4M3 ("e4m3fn": 1 sign bit, 4 exponent bits with
+// bias 7, 3 mantissa bits, largest finite value 448, no infinities), ties to
+// even, saturating: magnitudes at or above 448 give +-448. Returns the code.
+uint8_t rne_e4m3_sat_from_f64(double v) {
+    const uint8_t sign = std::signbit(v) ? 0x80u : 0x00u;
+    if (std::isnan(v)) return static_cast<uint8_t>(sign | 0x7Fu);
+    const double a = std::fabs(v);
+    if (a >= 448.0) return static_cast<uint8_t>(sign | 0x7Eu);
+    if (a == 0.0) return sign;
+    int ex = 0;
+    (void)std::frexp(a, &ex);
+    int lead = ex - 1;          // a in [2^lead, 2^(lead+1))
+    if (lead < -6) lead = -6;   // below the smallest normal 2^-6 the spacing is 2^-9
+    const int qexp = lead - 3;  // spacing of E4M3 values near a
+    const double n = std::ldexp(a, -qexp);
+    const double fl = std::floor(n);
+    const double frac = n - fl;
+    double r;
+    if (frac > 0.5) {
+        r = fl + 1.0;
+    } else if (frac < 0.5) {
+        r = fl;
+    } else {
+        r = (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    }
+    const double y = std::ldexp(r, qexp);  // an E4M3 value (at most 448 here)
+    if (y == 0.0) return sign;
+    int ey = 0;
+    (void)std::frexp(y, &ey);
+    const int e = ey - 1;
+    if (e < -6) {  // subnormal: y = m * 2^-9
+        const int m = static_cast<int>(std::ldexp(y, 9));
+        return static_cast<uint8_t>(sign | m);
+    }
+    const int m = static_cast<int>((std::ldexp(y, -e) - 1.0) * 8.0);
+    return static_cast<uint8_t>(sign | ((e + 7) << 3) | m);
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +227,37 @@ int mfr_oracle_residual_rmsnorm(const uint16_t* x, const uint16_t* residual,
         }
     }
     return MFR_ORACLE_OK;
+}
+
+// Dynamic per-token FP8 quantisation of rows of (unrounded) values: the
+// activation format of an FP8 GEMM with dynamic per-token activation scales
+// ("Port the validated GLM-5.2 H200 production path to latest vLLM", Prepared
+// experiment branches: the attention projections whose input is this norm's
+// output run FP8 GEMMs with static per-tensor weight scales and dynamic
+// per-token activation scales). Per row: amax = max |y|, scale = amax / 448
+// (1 when amax is 0), code = E4M3(y / scale) rounded to nearest even.
+//   y       [T, H] double   values to quantise (e.g. normed_exact)
+//   codes   [T, H] uint8    (out) E4M3 codes
+//   scales  [T]    double   (out) per-row scale; y ~= E4M3 value * scale
+//   scaled  [T, H] double   (out, optional) y / scale before rounding
+void mfr_oracle_fp8_quantize_rows(const double* y, int64_t T, int64_t H, uint8_t* codes,
+                                  double* scales, double* scaled) {
+    for (int64_t t = 0; t < T; ++t) {
+        double amax = 0.0;
+        for (int64_t h = 0; h < H; ++h) amax = std::fmax(amax, std::fabs(y[t * H + h]));
+        const double sc = amax > 0.0 ? amax / 448.0 : 1.0;
+        scales[t] = sc;
+        for (int64_t h = 0; h < H; ++h) {
+            const double v = y[t * H + h] / sc;
+            codes[t * H + h] = rne_e4m3_sat_from_f64(v);
+            if (scaled) scaled[t * H + h] = v;
+        }
+    }
+}
+
+// Elementwise double -> E4M3 rounding (saturating), exported for the pins.
+void mfr_oracle_rne_e4m3_from_f64(const double* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = rne_e4m3_sat_from_f64(x[i]);
 }
 
 // Elementwise double -> bf16 rounding, exported so the rounding itself can be

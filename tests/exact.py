@@ -82,3 +82,35 @@ def bf16_values(bits):
     b = np.asarray(bits, dtype=np.uint16)
     with np.errstate(invalid="ignore"):
         return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+E4M3_MAX = Fraction(448)
+
+
+def e4m3_code_value(code):
+    """Exact value of a finite OCP E4M3 code (1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits; 0x7F / 0xFF are NaN and not accepted)."""
+    code = int(code) & 0xFF
+    sign = -1 if code & 0x80 else 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    assert not (e == 0xF and m == 0x7), "NaN code"
+    if e == 0:
+        return sign * Fraction(m, 8) * Fraction(1, 64)
+    return sign * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+def fraction_to_e4m3_code(q):
+    """Nearest E4M3 value to the exact rational q (ties to the even code),
+    saturating to +-448; by search over the 127 non-negative finite codes."""
+    q = Fraction(q)
+    sign = 0x80 if q < 0 else 0
+    a = -q if q < 0 else q
+    if a >= E4M3_MAX:
+        return sign | 0x7E
+    best = None
+    for code in range(0x7F):  # 0x00 .. 0x7E, increasing values
+        d = abs(e4m3_code_value(code) - a)
+        if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+            best = (d, code)
+    return sign | best[1]

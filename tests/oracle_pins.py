@@ -427,11 +427,99 @@ def pin_dense_equals_all_masked_finalize(o):
         assert np.array_equal(exact.bf16_values(a[k]), exact.bf16_values(b[k])), k
 
 
+# --------------------------------------------------------------------------
+# Dynamic per-token FP8 (E4M3) quantisation
+# --------------------------------------------------------------------------
+
+FINITE_E4M3 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def _e4m3_values(codes):
+    """Library decode of E4M3 codes: torch's float8_e4m3fn widening (exact)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def pin_e4m3_roundtrip(o):
+    """Every finite E4M3 value rounds back to its own code."""
+    vals = _e4m3_values(FINITE_E4M3)
+    assert np.array_equal(o.rne_e4m3_from_f64(vals), FINITE_E4M3)
+    assert [float(exact.e4m3_code_value(c)) for c in FINITE_E4M3] == vals.tolist()
+
+
+def pin_e4m3_midpoints_and_saturation(o):
+    lo = np.arange(0, 0x7E, dtype=np.uint8)  # neighbours lo, lo + 1 up to 448
+    a, c = _e4m3_values(lo), _e4m3_values(lo + 1)
+    m = (a + c) / 2.0
+    even = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(o.rne_e4m3_from_f64(m), even)
+    assert np.array_equal(o.rne_e4m3_from_f64(np.nextafter(m, np.inf)), lo + 1)
+    assert np.array_equal(o.rne_e4m3_from_f64(np.nextafter(m, 0.0)), lo)
+    assert np.array_equal(o.rne_e4m3_from_f64(-m), even | np.uint8(0x80))
+    sat = o.rne_e4m3_from_f64(np.array([448.0, 449.0, 464.0, 1e30, np.inf, -448.0, -1e30,
+                                        2.0 ** -10, -2.0 ** -10, 0.0, -0.0]))
+    assert sat.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x00, 0x80, 0x00, 0x80]
+
+
+def pin_e4m3_vs_torch(o):
+    """Library special case: inside +-448 (where torch's float8_e4m3fn
+    conversion does not need to saturate) the rounding equals torch's."""
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal(100_000) * np.exp2(rng.integers(-12, 9, size=100_000))).astype(np.float32)
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.rne_e4m3_from_f64(x.astype(np.float64)), ref)
+
+
+def pin_e4m3_vs_exact(o):
+    """Doubles that are not binary32 values, against exact rational search."""
+    rng = np.random.default_rng(19)
+    x = (rng.random(600) + 1.0) * np.exp2(rng.integers(-11, 10, size=600)) * np.where(
+        rng.random(600) < 0.5, -1.0, 1.0)
+    want = np.array([exact.fraction_to_e4m3_code(Fraction(float(v))) for v in x], dtype=np.uint8)
+    assert np.array_equal(o.rne_e4m3_from_f64(x), want)
+
+
+def pin_fp8_hand_case(o):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["fp8_cases"]
+    for case in cases:
+        codes, scales, _ = o.fp8_quantize_rows(np.asarray(case["y"], dtype=np.float64))
+        assert codes.tolist() == case["codes"], case["name"]
+        assert scales.tolist() == case["scale"], case["name"]
+
+
+def pin_fp8_quantize_properties(o):
+    """On real normed rows: scale = amax / 448; the largest element becomes
+    exactly +-448; every code is the nearest E4M3 value of y / scale; powers of
+    two of y leave the codes unchanged and scale the scale; an all-zero row has
+    scale 1 and zero codes."""
+    d = synth.config_inputs(1, 12)
+    y = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
+                           d["residual"], d["gamma"], d["eps"], d["scale"])["normed_exact"]
+    codes, scales, scaled = o.fp8_quantize_rows(y)
+    amax = np.abs(y).max(axis=1)
+    assert np.array_equal(scales, amax / 448.0)
+    arg = np.abs(y).argmax(axis=1)
+    top = codes[np.arange(len(arg)), arg]
+    assert np.all((top & 0x7F) == 0x7E)
+    vals = _e4m3_values(codes)
+    grid = _e4m3_values(FINITE_E4M3)
+    best = np.abs(scaled[..., None] - grid[None, None, :]).min(axis=-1)
+    assert np.all(np.abs(vals - scaled) <= best)
+    for j in (-3, 5):
+        c2, s2, _ = o.fp8_quantize_rows(y * 2.0 ** j)
+        assert np.array_equal(c2, codes) and np.array_equal(s2, scales * 2.0 ** j)
+    cz, sz, _ = o.fp8_quantize_rows(np.zeros((2, 16)))
+    assert np.all(cz == 0) and np.all(sz == 1.0)
+
+
 ALL_PINS = [
     pin_rne_roundtrip, pin_rne_midpoints, pin_rne_overflow_and_specials, pin_rne_vs_torch,
     pin_rne_vs_exact_random, pin_hand_cases, pin_bruteforce_exact, pin_sparse_matmul,
     pin_rms_norm_library, pin_closed_form_k1, pin_slot_permutation, pin_zero_routed,
     pin_scale_invariance, pin_unit_rms, pin_masked_nan_poison, pin_weight_zero_reads_row,
     pin_index_range, pin_dense_hand_case, pin_dense_bruteforce_exact, pin_dense_rms_norm_library,
-    pin_dense_equals_all_masked_finalize,
+    pin_dense_equals_all_masked_finalize, pin_e4m3_roundtrip, pin_e4m3_midpoints_and_saturation,
+    pin_e4m3_vs_torch, pin_e4m3_vs_exact, pin_fp8_hand_case, pin_fp8_quantize_properties,
 ]

@@ -36,8 +36,22 @@ MUTANTS = [
     ("dense_eps_outside_root", "std::sqrt(sumsq / static_cast<double>(H) + eps_d)",
      "(std::sqrt(sumsq / static_cast<double>(H)) + eps_d)"),
     ("dense_sum_not_mean", "sumsq / static_cast<double>(H) + eps_d", "sumsq + eps_d"),
-    ("dense_gamma_dropped", "const double y = s[h] / denom * bf16_bits_to_double(gamma[h]);\n            residual_out[t * H + h] = rne_bf16_from_f64(s[h]);\n            normed_out[t * H + h] = rne_bf16_from_f64(y);\n            if (s_exact) s_exact[t * H + h] = s[h];\n            if (normed_exact) normed_exact[t * H + h] = y;\n        }\n    }\n    return MFR_ORACLE_OK;\n}\n\n// Elementwise",
-     "const double y = s[h] / denom;\n            residual_out[t * H + h] = rne_bf16_from_f64(s[h]);\n            normed_out[t * H + h] = rne_bf16_from_f64(y);\n            if (s_exact) s_exact[t * H + h] = s[h];\n            if (normed_exact) normed_exact[t * H + h] = y;\n        }\n    }\n    return MFR_ORACLE_OK;\n}\n\n// Elementwise"),
+    ("dense_gamma_dropped",
+     "const double denom = std::sqrt(sumsq / static_cast<double>(H) + eps_d);\n"
+     "        for (int64_t h = 0; h < H; ++h) {\n"
+     "            const double y = s[h] / denom * bf16_bits_to_double(gamma[h]);",
+     "const double denom = std::sqrt(sumsq / static_cast<double>(H) + eps_d);\n"
+     "        for (int64_t h = 0; h < H; ++h) {\n"
+     "            const double y = s[h] / denom;"),
+    ("e4m3_ties_up",
+     "r = (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;\n    }\n    const double y = std::ldexp(r, qexp);  // an E4M3 value",
+     "r = fl + 1.0;\n    }\n    const double y = std::ldexp(r, qexp);  // an E4M3 value"),
+    ("e4m3_no_saturation", "if (a >= 448.0) return static_cast<uint8_t>(sign | 0x7Eu);", ""),
+    ("e4m3_fnuz_max", "amax > 0.0 ? amax / 448.0 : 1.0", "amax > 0.0 ? amax / 240.0 : 1.0"),
+    ("e4m3_bias_8", "((e + 7) << 3)", "((e + 8) << 3)"),
+    ("e4m3_subnormal_spacing", "if (lead < -6) lead = -6;", "if (lead < -7) lead = -7;"),
+    ("fp8_scale_from_first_element", "amax = std::fmax(amax, std::fabs(y[t * H + h]));",
+     "amax = std::fabs(y[t * H]);"),
 ]
 
 
