@@ -290,6 +290,41 @@ def dense_figures():
             "decode_T28_us": round(dec, 2)}
 
 
+def fp8_figures():
+    """The fused op with its normalised output as per-token FP8 (no bf16 normed
+    output): the 8192-token chunk (HBM-cold by size) and one 28-token decode
+    step inside a graph."""
+    import torch
+    import synth
+    import top_finalize_residual_amd as mfr
+
+    def caller(d):
+        dd = to_device(d)
+        T, K, H = d["T"], d["K"], d["H"]
+        ro = torch.empty_like(dd["residual"])
+        q = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((T,), dtype=torch.float32, device="cuda")
+        a = [dd[k].data_ptr() for k in ("expert_out", "perm_idx", "topk_w", "shared_out",
+                                        "residual", "gamma")]
+
+        def call():
+            rc = mfr.moe_finalize_rmsnorm_fp8_raw(*a, d["eps"], d["scale"], ro.data_ptr(), None,
+                                                  q.data_ptr(), sc.data_ptr(), T, H, K,
+                                                  torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(mfr.strerror(rc))
+        call.keep = (dd, ro, q, sc)
+        return call
+    d = synth.config_inputs(4, 8192)
+    nbytes = synth.fp8_algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    ms = time_calls([caller(d)], 60, 6)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    dec = time_graph([caller(synth.config_inputs(1, 28))], 100, 5) * 1e3
+    return {"prefill_T8192": {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes},
+            "decode_T28_us": round(dec, 2)}
+
+
 def deferred_overhead():
     """Host cost of the torch-facing deferred path at one decode step (T=28):
     eager calls through fused_add_rmsnorm (custom op dispatch + ctypes) and
@@ -386,6 +421,8 @@ def run_bench(args):
         rec["batch_512"] = graph_ceiling_batch()
         log("dense residual add + RMSNorm (no routed part)")
         rec["dense_residual_rmsnorm"] = dense_figures()
+        log("FP8 (E4M3 per-token) normalised output")
+        rec["fp8_output"] = fp8_figures()
         log("deferred-finalize torch path: host overhead")
         rec["deferred_path"] = deferred_overhead()
     if not args.no_cpu_baseline:

@@ -103,6 +103,34 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
                          uint16_t* residual_out, uint16_t* normed_out,
                          int64_t T, int64_t H, int64_t K, hipStream_t stream);
 
+/* The fused op with the normalised output also (or only) produced as dynamic
+ * per-token FP8, the activation format of the FP8 projection that consumes it
+ * ("Port the validated GLM-5.2 H200 production path to latest vLLM", Prepared
+ * experiment branches: the attention projections run FP8 GEMMs with static
+ * per-tensor weight scales and dynamic per-token activation scales). With y the
+ * fp32 normalised row (before any bf16 rounding):
+ *
+ *   amax             = max_h |y[h]|
+ *   fp8_scale[t]     = amax / 448                (1 for an all-zero row)
+ *   normed_fp8[t,h]  = E4M3(y[h] * 448 / amax)   (OCP E4M3: bias 7, 3 mantissa
+ *                      bits, round to nearest even, saturated to +-448)
+ *
+ * so y[h] ~= value(normed_fp8[t,h]) * fp8_scale[t]. Arguments as for
+ * moe_finalize_rmsnorm, plus:
+ *   normed_out   [T, H] bf16   optional: NULL skips the bf16 normed output
+ *   normed_fp8   [T, H] uint8  E4M3 codes, 8-byte aligned
+ *   fp8_scale    [T]    fp32   per-token scale, 4-byte aligned
+ * No output may overlap another output or any input (residual_out ==
+ * residual excepted). residual_out, and normed_out when given, are
+ * bit-identical to those of moe_finalize_rmsnorm with the same arguments. */
+int moe_finalize_rmsnorm_fp8(const uint16_t* expert_out, const int32_t* perm_idx,
+                             const float* topk_w, const uint16_t* shared_out,
+                             const uint16_t* residual, const uint16_t* gamma,
+                             float eps, float scale,
+                             uint16_t* residual_out, uint16_t* normed_out,
+                             uint8_t* normed_fp8, float* fp8_scale,
+                             int64_t T, int64_t H, int64_t K, hipStream_t stream);
+
 /* Dense residual add + RMSNorm: the same tail with no routed part, for the
  * layers whose row-parallel attention / MLP outputs, or the final main-model
  * and MTP norms, feed the residual stream ("Port the validated GLM-5.2 H200

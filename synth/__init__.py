@@ -166,6 +166,16 @@ def dense_inputs(T, H, *, eps=EPS, seed=BASE_SEED, spike_frac=0.0):
                 H=H, spike_rows=d["spike_rows"])
 
 
+def fp8_algorithmic_bytes(perm_idx, H, K, bf16_normed=False):
+    """The fused op writing its normalised output as FP8: the reads of
+    algorithmic_bytes, residual_out (2H), the E4M3 codes (H) and the scale (4)
+    per token, plus the bf16 normed output (2H) when it is also written."""
+    T = perm_idx.shape[0]
+    valid = int((np.asarray(perm_idx) >= 0).sum())
+    per_token_out = 2 * H + H + 4 + (2 * H if bf16_normed else 0)
+    return 2 * H * valid + 2 * (2 * H) * T + 8 * K * T + 2 * H + per_token_out * T
+
+
 def dense_algorithmic_bytes(T, H):
     """x, residual and both outputs (2H bytes each per token), plus gamma once."""
     return 8 * H * T + 2 * H

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
                  "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force",
-                 "residual_add_rmsnorm"):
+                 "residual_add_rmsnorm", "moe_finalize_rmsnorm_fp8"):
         assert want in names
 
 
@@ -182,3 +182,32 @@ def test_dense_validation():
     assert dense_call(residual_out=A + 4 * act + 16) == binding.MFR_ERR_ALIAS  # partial overlap
     assert dense_call(residual_out=A + 8 * act) == binding.MFR_ERR_ALIAS  # on gamma
     assert mfr.residual_add_rmsnorm_raw(None, None, None, 1e-6, None, None, 0, H, None) == binding.MFR_OK
+
+
+def fp8_call(T_=T, H_=H, K_=K, **over):
+    act = T * H * 2
+    p = dict(_ptrs(), normed_fp8=A + 80 * act, fp8_scale=A + 90 * act)
+    p.update(over)
+    return mfr.moe_finalize_rmsnorm_fp8_raw(p["expert_out"], p["perm_idx"], p["topk_w"],
+                                            p["shared_out"], p["residual"], p["gamma"], 1e-6, 2.5,
+                                            p["residual_out"], p["normed_out"], p["normed_fp8"],
+                                            p["fp8_scale"], T_, H_, K_, None)
+
+
+def test_fp8_validation():
+    act = T * H * 2
+    base = dict(_ptrs(), normed_fp8=A + 80 * act, fp8_scale=A + 90 * act)
+    for name in ("expert_out", "perm_idx", "topk_w", "shared_out", "residual", "gamma",
+                 "residual_out", "normed_fp8", "fp8_scale"):
+        assert fp8_call(**{name: None}) == binding.MFR_ERR_NULL, name
+    assert fp8_call(normed_fp8=base["normed_fp8"] + 4) == binding.MFR_ERR_ALIGN
+    assert fp8_call(fp8_scale=base["fp8_scale"] + 2) == binding.MFR_ERR_ALIGN
+    assert fp8_call(normed_out=base["normed_out"] + 8) == binding.MFR_ERR_ALIGN
+    assert fp8_call(T_=4, H_=12) == binding.MFR_ERR_SHAPE
+    # codes on top of the residual output, the scale inside the codes, codes on an input
+    assert fp8_call(normed_fp8=base["residual_out"]) == binding.MFR_ERR_ALIAS
+    assert fp8_call(fp8_scale=base["normed_fp8"] + 64) == binding.MFR_ERR_ALIAS
+    assert fp8_call(normed_fp8=base["shared_out"]) == binding.MFR_ERR_ALIAS
+    assert fp8_call(normed_out=base["normed_fp8"]) == binding.MFR_ERR_ALIAS
+    # without the optional bf16 output, its pointer is not examined
+    assert fp8_call(T_=0, normed_out=None) == binding.MFR_OK

@@ -1,0 +1,127 @@
+"""GPU parity of the fused op's dynamic per-token FP8 output against the oracle
+(finalize, then per-token E4M3 quantisation of the exact normed rows).
+
+Codes are compared exactly, except next to a rounding tie: the GPU forms y and
+the scale in fp32, so its y / scale carries the fp32 error of the sum s (the
+same 1e-6 absolute floor the bf16 gate allows, carried through the
+normalisation and the scale) plus a relative 2^-18. Where the exact y / scale
+lies that close to the midpoint between two E4M3 neighbours, either is a
+correct rounding and the GPU's code may be the other one. Scales agree to
+fp32 accuracy."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_finalize_residual_amd as mfr
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SCALE_REL = 2.0 ** -20
+TIE_REL = 2.0 ** -18
+
+
+def e4m3_key(codes):
+    """Monotone integer key of E4M3 codes (+0 and -0 map to 0)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_values(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def run_fp8(dd, d, path=0, vpt=0, store=0, bf16_normed=False):
+    with gu.forced(path, vpt, store):
+        r, q, sc, n = mfr.moe_finalize_rmsnorm_fp8(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
+                                                   dd["shared_out"], dd["residual"], dd["gamma"],
+                                                   d["eps"], d["scale"], bf16_normed=bf16_normed)
+    torch.cuda.synchronize()
+    return (gu.host_u16(r), q.view(torch.uint8).cpu().numpy(), sc.cpu().numpy().astype(np.float64),
+            None if n is None else gu.host_u16(n))
+
+
+def check_fp8(codes, scales, ref, gamma, eps):
+    """ref: the oracle's finalize outputs (s, normed_exact) for these rows."""
+    normed_exact = ref["normed_exact"]
+    want, want_scale, scaled = oracle.fp8_quantize_rows(normed_exact)
+    assert np.all(np.abs(scales - want_scale) <= SCALE_REL * want_scale), "scale"
+    diff = np.abs(e4m3_key(codes) - e4m3_key(want))
+    assert diff.max(initial=0) <= 1, f"codes {int(diff.max())} steps apart"
+    if diff.any():
+        # the exact value must sit at the midpoint of the two codes, within the
+        # error the GPU's fp32 y / scale may carry there
+        s = ref["s"]
+        rstd = 1.0 / np.sqrt(np.mean(s * s, axis=1, keepdims=True) + eps)
+        g = np.abs(gu.bf16_f64(gamma))[None, :]
+        tol = gu.ABS * rstd * g / want_scale[:, None] + TIE_REL * np.abs(scaled)
+        a, b = e4m3_values(codes[diff == 1]), e4m3_values(want[diff == 1])
+        v = scaled[diff == 1]
+        assert np.all(np.abs(v - (a + b) / 2) <= tol[diff == 1]), "code differs away from a tie"
+    assert not np.any((codes & 0x7F) == 0x7F), "NaN code"
+    return want
+
+
+CASES = [(0, 4), (1, 1), (1, 28), (1, 64), (2, 64), (3, 512)]
+
+
+@pytest.mark.parametrize("path", [0, mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["auto", "token", "stream"])
+@pytest.mark.parametrize("cfg,T", CASES, ids=[f"cfg{c}-T{t}" for c, t in CASES])
+def test_fp8_parity(cfg, T, path):
+    d = synth.config_inputs(cfg, T)
+    dd = gu.to_device(d)
+    r, q, sc, n = run_fp8(dd, d, path=path, bf16_normed=True)
+    ref = gu.oracle_for(d)
+    check_fp8(q, sc, ref, d["gamma"], d["eps"])
+    # the bf16 outputs are those of the plain call
+    r0, n0 = gu.run(dd, d["eps"], d["scale"], path=path)
+    assert np.array_equal(r, r0) and np.array_equal(n, n0)
+
+
+def test_fp8_without_bf16_normed_and_store_policies():
+    d = synth.config_inputs(3, 512)
+    dd = gu.to_device(d)
+    r1, q1, s1, n1 = run_fp8(dd, d)
+    assert n1 is None
+    for store in (mfr.STORE_WRITE_BACK, mfr.STORE_WRITE_THROUGH):
+        r2, q2, s2, _ = run_fp8(dd, d, store=store, bf16_normed=True)
+        assert np.array_equal(r1, r2) and np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    check_fp8(q1, s1, gu.oracle_for(d), d["gamma"], d["eps"])
+
+
+def test_fp8_prefill_full_size_sampled():
+    d = synth.config_inputs(4, 8192)
+    dd = gu.to_device(d)
+    r, q, sc, _ = run_fp8(dd, d)
+    rng = np.random.default_rng(7)
+    tokens = np.unique(np.concatenate([d["spike_rows"], rng.choice(8192, 150, replace=False)]))
+    ref = gu.oracle_for(d, tokens)
+    check_fp8(q[tokens], sc[tokens], ref, d["gamma"], d["eps"])
+    gu.assert_gate(r[tokens], ref["s"], ref["residual_out"], "residual_out")
+
+
+RAGGED = [(3, 16, 2), (7, 1000, 5), (33, 2056, 9), (17, 6152, 16), (2, 16384, 16)]
+
+
+@pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
+@pytest.mark.parametrize("T,H,K", RAGGED, ids=[f"T{t}-H{h}-K{k}" for t, h, k in RAGGED])
+def test_fp8_ragged(T, H, K, path):
+    d = synth.generate(T, H, K, scale=2.5, mask_frac=0.1, seed=700 + T + H)
+    dd = gu.to_device(d)
+    r, q, sc, _ = run_fp8(dd, d, path=path)
+    check_fp8(q, sc, gu.oracle_for(d), d["gamma"], d["eps"])
+
+
+def test_fp8_zero_row():
+    """A token whose sum is exactly zero: scale 1, every code zero."""
+    d = synth.generate(4, 2048, 8, scale=1.0, seed=71)
+    d["topk_w"][1] = 0.0
+    d["residual"][1] = d["shared_out"][1] ^ np.uint16(0x8000)
+    dd = gu.to_device(d)
+    r, q, sc, _ = run_fp8(dd, d)
+    assert sc[1] == 1.0 and np.all(e4m3_key(q[1]) == 0)
+    check_fp8(q, sc, gu.oracle_for(d), d["gamma"], d["eps"])

@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     STORE_WRITE_THROUGH,
     moe_finalize_rmsnorm,
     moe_finalize_rmsnorm_force,
+    moe_finalize_rmsnorm_fp8,
+    moe_finalize_rmsnorm_fp8_raw,
     moe_finalize_rmsnorm_path,
     moe_finalize_rmsnorm_raw,
     residual_add_rmsnorm,

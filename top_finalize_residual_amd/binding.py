@@ -43,6 +43,9 @@ _lib.moe_finalize_rmsnorm_path.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_path.argtypes = [_i64, _i64, _i64]
 _lib.moe_finalize_rmsnorm_strerror.restype = ctypes.c_char_p
 _lib.moe_finalize_rmsnorm_strerror.argtypes = [ctypes.c_int]
+_lib.moe_finalize_rmsnorm_fp8.restype = ctypes.c_int
+_lib.moe_finalize_rmsnorm_fp8.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_float, ctypes.c_float,
+                                          _p, _p, _p, _p, _i64, _i64, _i64, _p]
 _lib.residual_add_rmsnorm.restype = ctypes.c_int
 _lib.residual_add_rmsnorm.argtypes = [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _p]
 _lib.moe_finalize_rmsnorm_force.restype = ctypes.c_int
@@ -173,3 +176,60 @@ def residual_add_rmsnorm(x, residual, gamma, eps, residual_out=None, normed_out=
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_out
+
+
+def moe_finalize_rmsnorm_fp8_raw(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
+                                 scale, residual_out, normed_out, normed_fp8, fp8_scale, T, H, K,
+                                 stream):
+    """Direct C call with integer addresses (normed_out may be 0/None); returns the status."""
+    return _lib.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
+                                         float(eps), float(scale), residual_out, normed_out or None,
+                                         normed_fp8, fp8_scale, int(T), int(H), int(K), stream)
+
+
+def moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
+                             residual_out=None, normed_fp8=None, fp8_scale=None, bf16_normed=False,
+                             normed_out=None, stream=None):
+    """The fused op with the normalised output as dynamic per-token FP8 (E4M3).
+
+    Returns (residual_out, normed_fp8 [T, H] torch.float8_e4m3fn, fp8_scale [T]
+    float32, normed_out or None). The bf16 normed output is written only when
+    bf16_normed is true or normed_out is given.
+    """
+    _check(expert_out, "expert_out", torch.bfloat16, 2)
+    _check(perm_idx, "perm_idx", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(shared_out, "shared_out", torch.bfloat16, 2)
+    _check(residual, "residual", torch.bfloat16, 2)
+    _check(gamma, "gamma", torch.bfloat16, 1)
+    T, K = perm_idx.shape
+    H = gamma.shape[0]
+    if expert_out.shape[1] != H or tuple(shared_out.shape) != (T, H) or \
+            tuple(residual.shape) != (T, H) or tuple(topk_w.shape) != (T, K):
+        raise ValueError("inconsistent shapes")
+    dev = residual.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if normed_fp8 is None:
+        normed_fp8 = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev)
+    if fp8_scale is None:
+        fp8_scale = torch.empty((T,), dtype=torch.float32, device=dev)
+    if normed_out is None and bf16_normed:
+        normed_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(residual_out, "residual_out", torch.bfloat16, 2)
+    if normed_fp8.dtype not in (torch.float8_e4m3fn, torch.uint8) or not normed_fp8.is_cuda or \
+            not normed_fp8.is_contiguous() or tuple(normed_fp8.shape) != (T, H):
+        raise ValueError("normed_fp8 must be a contiguous [T, H] float8_e4m3fn (or uint8) GPU tensor")
+    _check(fp8_scale, "fp8_scale", torch.float32, 1)
+    if normed_out is not None:
+        _check(normed_out, "normed_out", torch.bfloat16, 2)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = _lib.moe_finalize_rmsnorm_fp8(
+        expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
+        residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale), residual_out.data_ptr(),
+        normed_out.data_ptr() if normed_out is not None else None, normed_fp8.data_ptr(),
+        fp8_scale.data_ptr(), T, H, K, stream.cuda_stream)
+    if rc != MFR_OK:
+        raise MFRError(rc)
+    return residual_out, normed_fp8, fp8_scale, normed_out

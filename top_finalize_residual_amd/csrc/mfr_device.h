@@ -13,6 +13,7 @@
 namespace mfr {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -64,6 +65,24 @@ __device__ __forceinline__ void buf_store(u32x4 v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, AUX);
 }
 
+template <int AUX>
+__device__ __forceinline__ void buf_store_b64(u32x2 v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ void buf_store_b32(float v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, AUX);
+}
+
+// Clamp to the finite OCP E4M3 range [-448, 448] before the hardware
+// conversion, keeping NaN as NaN (the conversion would otherwise turn values
+// just above 448 into NaN).
+__device__ __forceinline__ float sat_e4m3(float v) {
+    const float c = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+    return v != v ? v : c;
+}
+
 // One DPP move of a float within a row of 16 lanes (every lane active).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -84,6 +103,20 @@ __device__ __forceinline__ float wave_sum(float x) {
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
     return (r0 + r1) + (r2 + r3);
+}
+
+// Maximum over the 64 lanes of a wave, returned to every lane; the same DPP
+// tree as wave_sum with max in place of add.
+__device__ __forceinline__ float wave_max(float x) {
+    x = __builtin_fmaxf(x, dpp<0xB1>(x));
+    x = __builtin_fmaxf(x, dpp<0x4E>(x));
+    x = __builtin_fmaxf(x, dpp<0x141>(x));
+    x = __builtin_fmaxf(x, dpp<0x140>(x));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
 }
 
 }  // namespace mfr

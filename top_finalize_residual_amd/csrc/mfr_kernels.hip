@@ -62,7 +62,14 @@ struct Params {
     float h_f;  // H as float (exact: H <= 16384)
     int V;      // 16-byte vectors per row, H / 8
     int K;
+    uint8_t* normed_fp8;  // [T, H] E4M3 codes (FP8 output modes only)
+    float* fp8_scale;     // [T] per-token scales (FP8 output modes only)
 };
+
+// What the normalisation writes: the bf16 normed row, the per-token FP8
+// (E4M3) row with its scale, or both.
+enum OutMode { kOutBf16 = 0, kOutFp8 = 1, kOutBoth = 2 };
+constexpr float kE4m3Max = 448.0f;  // largest finite OCP E4M3 value
 
 constexpr int MAX_WAVES = 16;  // 1024 threads
 
@@ -124,7 +131,7 @@ __device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&id
 // every row; offsets at or past the row end (a ragged last tile) fall outside
 // the descriptors' range, so their loads return zero and their stores are
 // dropped by the hardware.
-template <int VPT, int KT, int OUT_AUX>
+template <int VPT, int KT, int OUT_AUX, int QM>
 __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t, float* red) {
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
@@ -205,18 +212,59 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     for (int w = 0; w < nw; ++w) tot += red[w];
     const float rstd = 1.0f / __builtin_sqrtf(tot / p.h_f + p.eps);
 
-    const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
+    float y[VPT][8];
+    float amax = 0.0f;  // of this lane's normed values (FP8 modes)
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        float y[8];
+    for (int j = 0; j < VPT; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (acc[j][e] * rstd) * vec_elem(gm[j], e);
-        u32x4 o;
-        o.x = pack_bf16x2(y[0], y[1]);
-        o.y = pack_bf16x2(y[2], y[3]);
-        o.z = pack_bf16x2(y[4], y[5]);
-        o.w = pack_bf16x2(y[6], y[7]);
-        buf_store<OUT_AUX>(o, no_r, off[j]);
+        for (int e = 0; e < 8; ++e) {
+            y[j][e] = (acc[j][e] * rstd) * vec_elem(gm[j], e);
+            if (QM != kOutBf16) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[j][e]));
+        }
+
+    if (QM != kOutFp8) {
+        const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            u32x4 o;
+            o.x = pack_bf16x2(y[j][0], y[j][1]);
+            o.y = pack_bf16x2(y[j][2], y[j][3]);
+            o.z = pack_bf16x2(y[j][4], y[j][5]);
+            o.w = pack_bf16x2(y[j][6], y[j][7]);
+            buf_store<OUT_AUX>(o, no_r, off[j]);
+        }
+    }
+
+    if (QM != kOutBf16) {
+        // Dynamic per-token FP8: a second row reduction for max |y| (its own
+        // LDS slots, so it cannot race the sum just read), then
+        // scale = amax / 448 and codes = E4M3(y * 448 / amax), saturated.
+        const float wmax = wave_max(amax);
+        if ((tid & 63) == 0) red[MAX_WAVES + (tid >> 6)] = wmax;
+        __syncthreads();
+        float rmax = 0.0f;
+        for (int w = 0; w < nw; ++w) rmax = __builtin_fmaxf(rmax, red[MAX_WAVES + w]);
+        const bool zero_row = !(rmax > 0.0f);
+        const float qscale = zero_row ? 1.0f : rmax / kE4m3Max;
+        const float inv = zero_row ? 0.0f : kE4m3Max / rmax;
+        const rsrc_t q_r = make_rsrc(p.normed_fp8 + t * static_cast<int64_t>(p.V) * 8,
+                                     static_cast<uint32_t>(p.V) * 8u);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = sat_e4m3(y[j][e] * inv);
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+            u32x2 q = {static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
+            buf_store_b64<OUT_AUX>(q, q_r, off[j] >> 1);  // 8 code bytes per 16 bf16 bytes
+        }
+        if (tid == 0) {
+            const rsrc_t s_r = make_rsrc(p.fp8_scale + t, 4u);
+            buf_store_b32<kAuxDefault>(qscale, s_r, 0u);
+        }
     }
 }
 
@@ -227,12 +275,13 @@ struct Bound {
     static constexpr int kThreads = VPT == 1 ? 1024 : 512;
 };
 
-// One workgroup per token. OUT_AUX is the cache policy of the two output
-// stores (write-back, or write-through for outputs larger than the L2).
-template <int VPT, int KT, int OUT_AUX>
+// One workgroup per token. OUT_AUX is the cache policy of the output stores
+// (write-back, or write-through for outputs larger than the L2); QM the
+// OutMode of the normalised output.
+template <int VPT, int KT, int OUT_AUX, int QM>
 __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(Params p) {
-    __shared__ float red[MAX_WAVES];
-    finalize_token<VPT, KT, OUT_AUX>(p, static_cast<int64_t>(blockIdx.x), red);
+    __shared__ float red[2 * MAX_WAVES];  // row sums, then row maxima (FP8 modes)
+    finalize_token<VPT, KT, OUT_AUX, QM>(p, static_cast<int64_t>(blockIdx.x), red);
 }
 
 }  // namespace mfr
@@ -306,63 +355,77 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-template <int VPT, int KT>
+template <int VPT, int KT, int QM>
 const void* pick_store(bool wt) {
-    return wt ? reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough>)
-              : reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut>);
+    return wt ? reinterpret_cast<const void*>(
+                    &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough, QM>)
+              : reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut, QM>);
 }
 
 // Routing variant of a launch: exactly eight slots, any K, or no routed part.
 enum Variant { kTop8 = 8, kAnyK = 0, kDense = -1 };
 
-template <int VPT>
-const void* pick(Variant v, bool wt) {
+template <int VPT, int QM>
+const void* pick_variant(Variant v, bool wt) {
     switch (v) {
-        case kTop8: return pick_store<VPT, 8>(wt);
-        case kAnyK: return pick_store<VPT, 0>(wt);
-        default: return pick_store<VPT, -1>(wt);
+        case kTop8: return pick_store<VPT, 8, QM>(wt);
+        case kAnyK: return pick_store<VPT, 0, QM>(wt);
+        default: return pick_store<VPT, -1, QM>(wt);
     }
 }
 
-// Kernel address for (vectors per thread, routing variant, write-through outputs).
-const void* kernel_for(int vpt, Variant v, bool wt) {
+template <int VPT>
+const void* pick(Variant v, bool wt, int qm) {
+    switch (qm) {
+        case mfr::kOutFp8: return pick_variant<VPT, mfr::kOutFp8>(v, wt);
+        case mfr::kOutBoth: return pick_variant<VPT, mfr::kOutBoth>(v, wt);
+        default: return pick_variant<VPT, mfr::kOutBf16>(v, wt);
+    }
+}
+
+// Kernel address for (vectors per thread, routing variant, write-through
+// outputs, output mode).
+const void* kernel_for(int vpt, Variant v, bool wt, int qm) {
     switch (vpt) {
-        case 1: return pick<1>(v, wt);
-        case 2: return pick<2>(v, wt);
-        case 3: return pick<3>(v, wt);
-        default: return pick<4>(v, wt);
+        case 1: return pick<1>(v, wt, qm);
+        case 2: return pick<2>(v, wt, qm);
+        case 3: return pick<3>(v, wt, qm);
+        default: return pick<4>(v, wt, qm);
     }
 }
 
-// Output checks shared by both entry points: residual_out may be exactly
-// residual; otherwise neither output may overlap an input or the other output.
-// `others` are the remaining inputs with their byte extents.
+// Aliasing rule shared by the entry points: no output may overlap another
+// output or any input, except that residual_out may be exactly residual (the
+// in-place residual update). Extents are in bytes; an empty extent never
+// overlaps.
 struct Extent {
     const void* p;
     uint64_t n;
 };
 
-int check_outputs(const void* residual_out, const void* normed_out, const void* residual,
-                  uint64_t act, const Extent* others, int n_others) {
-    if (residual_out != residual && overlaps(residual_out, act, residual, act)) return MFR_ERR_ALIAS;
-    if (overlaps(residual_out, act, normed_out, act) || overlaps(normed_out, act, residual, act))
-        return MFR_ERR_ALIAS;
-    for (int i = 0; i < n_others; ++i)
-        if (overlaps(residual_out, act, others[i].p, others[i].n) ||
-            overlaps(normed_out, act, others[i].p, others[i].n))
-            return MFR_ERR_ALIAS;
+int check_aliasing(const Extent* outs, int n_out, const Extent* ins, int n_in,
+                   const void* residual_out, const void* residual) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return MFR_ERR_ALIAS;
+        for (int j = 0; j < n_in; ++j) {
+            const bool in_place = outs[i].p == residual_out && ins[j].p == residual &&
+                                  residual_out == residual && outs[i].n == ins[j].n;
+            if (!in_place && overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return MFR_ERR_ALIAS;
+        }
+    }
     return MFR_OK;
 }
 
 // Fills the shape fields, picks the launch shape and enqueues the kernel.
-int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, hipStream_t stream) {
+int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t stream) {
     p.T = T;
     p.h_f = static_cast<float>(H);
     p.V = static_cast<int>(H / 8);
     const int path = choose_path(T);
     const int vpt = choose_vpt(path, p.V);
     const int nt = threads_for(p.V, vpt);
-    const void* kern = kernel_for(vpt, v, write_through(path, T, H));
+    const void* kern = kernel_for(vpt, v, write_through(path, T, H), qm);
     void* args[] = {&p};
     const hipError_t e =
         hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
@@ -394,9 +457,10 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     const uint64_t meta = static_cast<uint64_t>(T) * K * 4;
     // expert_out's extent is unknown (R is not passed): only its first 16
     // bytes are checked.
-    const Extent others[] = {{shared_out, act}, {gamma, static_cast<uint64_t>(H) * 2},
-                             {perm_idx, meta}, {topk_w, meta}, {expert_out, 16}};
-    const int rc = check_outputs(residual_out, normed_out, residual, act, others, 5);
+    const Extent outs[] = {{residual_out, act}, {normed_out, act}};
+    const Extent ins[] = {{residual, act}, {shared_out, act}, {gamma, static_cast<uint64_t>(H) * 2},
+                          {perm_idx, meta}, {topk_w, meta}, {expert_out, 16}};
+    const int rc = check_aliasing(outs, 2, ins, 6, residual_out, residual);
     if (rc != MFR_OK) return rc;
 
     mfr::Params p;
@@ -411,7 +475,53 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     p.eps = eps;
     p.scale = scale;
     p.K = static_cast<int>(K);
-    return launch(p, T, H, K == 8 ? kTop8 : kAnyK, stream);
+    return launch(p, T, H, K == 8 ? kTop8 : kAnyK, mfr::kOutBf16, stream);
+}
+
+int moe_finalize_rmsnorm_fp8(const uint16_t* expert_out, const int32_t* perm_idx,
+                             const float* topk_w, const uint16_t* shared_out,
+                             const uint16_t* residual, const uint16_t* gamma, float eps,
+                             float scale, uint16_t* residual_out, uint16_t* normed_out,
+                             uint8_t* normed_fp8, float* fp8_scale, int64_t T, int64_t H,
+                             int64_t K, hipStream_t stream) {
+    if (!shape_ok(T, H, K)) return MFR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(scale)) return MFR_ERR_SCALAR;
+    if (T == 0) return MFR_OK;
+    if (!expert_out || !perm_idx || !topk_w || !shared_out || !residual || !gamma ||
+        !residual_out || !normed_fp8 || !fp8_scale)
+        return MFR_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(shared_out, 16) || !aligned(residual, 16) ||
+        !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+        (normed_out && !aligned(normed_out, 16)) || !aligned(normed_fp8, 8) ||
+        !aligned(fp8_scale, 4) || !aligned(perm_idx, 4) || !aligned(topk_w, 4))
+        return MFR_ERR_ALIGN;
+    const uint64_t act = static_cast<uint64_t>(T) * H * 2;
+    const uint64_t meta = static_cast<uint64_t>(T) * K * 4;
+    const Extent outs[] = {{residual_out, act},
+                           {normed_fp8, static_cast<uint64_t>(T) * H},
+                           {fp8_scale, static_cast<uint64_t>(T) * 4},
+                           {normed_out, normed_out ? act : 0}};
+    const Extent ins[] = {{residual, act}, {shared_out, act}, {gamma, static_cast<uint64_t>(H) * 2},
+                          {perm_idx, meta}, {topk_w, meta}, {expert_out, 16}};
+    const int rc = check_aliasing(outs, 4, ins, 6, residual_out, residual);
+    if (rc != MFR_OK) return rc;
+
+    mfr::Params p = {};
+    p.expert_out = reinterpret_cast<const mfr::u32x4*>(expert_out);
+    p.perm_idx = perm_idx;
+    p.topk_w = topk_w;
+    p.shared_out = reinterpret_cast<const mfr::u32x4*>(shared_out);
+    p.residual = reinterpret_cast<const mfr::u32x4*>(residual);
+    p.gamma = reinterpret_cast<const mfr::u32x4*>(gamma);
+    p.residual_out = reinterpret_cast<mfr::u32x4*>(residual_out);
+    p.normed_out = reinterpret_cast<mfr::u32x4*>(normed_out);
+    p.normed_fp8 = normed_fp8;
+    p.fp8_scale = fp8_scale;
+    p.eps = eps;
+    p.scale = scale;
+    p.K = static_cast<int>(K);
+    return launch(p, T, H, K == 8 ? kTop8 : kAnyK, normed_out ? mfr::kOutBoth : mfr::kOutFp8,
+                  stream);
 }
 
 int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
@@ -425,8 +535,9 @@ int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint
         !aligned(residual_out, 16) || !aligned(normed_out, 16))
         return MFR_ERR_ALIGN;
     const uint64_t act = static_cast<uint64_t>(T) * H * 2;
-    const Extent others[] = {{x, act}, {gamma, static_cast<uint64_t>(H) * 2}};
-    const int rc = check_outputs(residual_out, normed_out, residual, act, others, 2);
+    const Extent outs[] = {{residual_out, act}, {normed_out, act}};
+    const Extent ins[] = {{residual, act}, {x, act}, {gamma, static_cast<uint64_t>(H) * 2}};
+    const int rc = check_aliasing(outs, 2, ins, 3, residual_out, residual);
     if (rc != MFR_OK) return rc;
 
     mfr::Params p = {};
@@ -438,7 +549,7 @@ int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint
     p.eps = eps;
     p.scale = 1.0f;
     p.K = 0;
-    return launch(p, T, H, kDense, stream);
+    return launch(p, T, H, kDense, mfr::kOutBf16, stream);
 }
 
 int moe_finalize_rmsnorm_path(int64_t T, int64_t H, int64_t K) {
