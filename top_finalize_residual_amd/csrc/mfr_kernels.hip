@@ -182,9 +182,10 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     }
 
     // s = (routed + shared) + residual (dense: x + residual); residual_out =
-    // bf16(s); per-lane sum of squares.
+    // bf16(s); per-lane sum of squares, and (FP8 modes) per-lane max |s * gamma|.
     const rsrc_t ro_r = make_rsrc(p.residual_out + trow, rowbytes);
     float ss = 0.0f;
+    float mg = 0.0f;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
 #pragma unroll
@@ -194,6 +195,8 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
             else
                 acc[j][e] = (acc[j][e] + vec_elem(sh[j], e)) + vec_elem(rs[j], e);
             ss = __builtin_fmaf(acc[j][e], acc[j][e], ss);
+            if (QM != kOutBf16)
+                mg = __builtin_fmaxf(mg, __builtin_fabsf(acc[j][e] * vec_elem(gm[j], e)));
         }
         u32x4 o;
         o.x = pack_bf16x2(acc[j][0], acc[j][1]);
@@ -203,24 +206,29 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
         buf_store<OUT_AUX>(o, ro_r, off[j]);
     }
 
-    // Row reduction: wave tree, then the waves' partial sums in order.
+    // Row reduction: wave tree, then the waves' partial sums in order. The FP8
+    // modes reduce max |s * gamma| alongside, through the same exchange and
+    // barrier: since rstd > 0, max |y| = rstd * max |s * gamma|.
     const float wsum = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = wsum;
+    const float wmg = QM != kOutBf16 ? wave_max(mg) : 0.0f;
+    if ((tid & 63) == 0) {
+        red[tid >> 6] = wsum;
+        if (QM != kOutBf16) red[MAX_WAVES + (tid >> 6)] = wmg;
+    }
     __syncthreads();
     float tot = 0.0f;
+    float rmg = 0.0f;
     const int nw = nt >> 6;
     for (int w = 0; w < nw; ++w) tot += red[w];
+    if (QM != kOutBf16)
+        for (int w = 0; w < nw; ++w) rmg = __builtin_fmaxf(rmg, red[MAX_WAVES + w]);
     const float rstd = 1.0f / __builtin_sqrtf(tot / p.h_f + p.eps);
 
     float y[VPT][8];
-    float amax = 0.0f;  // of this lane's normed values (FP8 modes)
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            y[j][e] = (acc[j][e] * rstd) * vec_elem(gm[j], e);
-            if (QM != kOutBf16) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[j][e]));
-        }
+        for (int e = 0; e < 8; ++e) y[j][e] = (acc[j][e] * rstd) * vec_elem(gm[j], e);
 
     if (QM != kOutFp8) {
         const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
@@ -236,14 +244,10 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     }
 
     if (QM != kOutBf16) {
-        // Dynamic per-token FP8: a second row reduction for max |y| (its own
-        // LDS slots, so it cannot race the sum just read), then
-        // scale = amax / 448 and codes = E4M3(y * 448 / amax), saturated.
-        const float wmax = wave_max(amax);
-        if ((tid & 63) == 0) red[MAX_WAVES + (tid >> 6)] = wmax;
-        __syncthreads();
-        float rmax = 0.0f;
-        for (int w = 0; w < nw; ++w) rmax = __builtin_fmaxf(rmax, red[MAX_WAVES + w]);
+        // Dynamic per-token FP8: amax = max |y| = rstd * max |s * gamma|,
+        // scale = amax / 448, codes = E4M3(y * 448 / amax), saturated (the
+        // fp32 product can overshoot 448 by an ulp).
+        const float rmax = rmg * rstd;
         const bool zero_row = !(rmax > 0.0f);
         const float qscale = zero_row ? 1.0f : rmax / kE4m3Max;
         const float inv = zero_row ? 0.0f : kE4m3Max / rmax;
@@ -280,7 +284,7 @@ struct Bound {
 // OutMode of the normalised output.
 template <int VPT, int KT, int OUT_AUX, int QM>
 __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(Params p) {
-    __shared__ float red[2 * MAX_WAVES];  // row sums, then row maxima (FP8 modes)
+    __shared__ float red[2 * MAX_WAVES];  // per-wave row sums and (FP8 modes) row maxima
     finalize_token<VPT, KT, OUT_AUX, QM>(p, static_cast<int64_t>(blockIdx.x), red);
 }
 
