@@ -88,6 +88,9 @@ def make_caller(dd, eps, scale):
         rc = mfr.moe_finalize_rmsnorm_raw(*args, eps, scale, ro, no, T, H, K, s)
         if rc != 0:
             raise RuntimeError(mfr.strerror(rc))
+    # the closure holds raw addresses: keep every tensor it writes or reads alive
+    # for as long as the closure lives
+    call.keep = (dd, r_out, n_out)
     return call, (r_out, n_out)
 
 

@@ -467,7 +467,7 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     const int rc = check_aliasing(outs, 2, ins, 6, residual_out, residual);
     if (rc != MFR_OK) return rc;
 
-    mfr::Params p;
+    mfr::Params p = {};
     p.expert_out = reinterpret_cast<const mfr::u32x4*>(expert_out);
     p.perm_idx = perm_idx;
     p.topk_w = topk_w;
