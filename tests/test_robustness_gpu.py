@@ -1,0 +1,91 @@
+"""GPU robustness: concurrent callers on separate streams, argument errors
+raised through the binding, and zero-token calls of every entry point."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import top_finalize_residual_amd as mfr
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_concurrent_threads_and_streams():
+    """Four host threads, each with its own stream and inputs, launch
+    repeatedly at the same time; every result equals its single-threaded one."""
+    cases = [synth.generate(T, 2048 if i % 2 else 6144, 8, scale=2.5, seed=900 + i)
+             for i, T in enumerate((1, 28, 64, 512))]
+    devs = [gu.to_device(d) for d in cases]
+    want = [gu.run(dd, d["eps"], d["scale"]) for d, dd in zip(cases, devs)]
+    outs = [None] * len(cases)
+    errors = []
+
+    def worker(i):
+        try:
+            d, dd = cases[i], devs[i]
+            s = torch.cuda.Stream()
+            r = torch.empty_like(dd["residual"])
+            n = torch.empty_like(dd["residual"])
+            with torch.cuda.stream(s):
+                for _ in range(50):
+                    mfr.moe_finalize_rmsnorm(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
+                                             dd["shared_out"], dd["residual"], dd["gamma"],
+                                             d["eps"], d["scale"], residual_out=r, normed_out=n)
+            s.synchronize()
+            outs[i] = (gu.host_u16(r), gu.host_u16(n))
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for (r0, n0), (r1, n1) in zip(want, outs):
+        assert np.array_equal(r0, r1) and np.array_equal(n0, n1)
+
+
+def test_binding_rejects_bad_tensors_before_launch():
+    d = synth.generate(4, 2048, 8, seed=901)
+    dd = gu.to_device(d)
+    args = [dd[k] for k in ("expert_out", "perm_idx", "topk_w", "shared_out", "residual", "gamma")]
+    # a bf16 view one element in: 2-byte aligned, refused by the library
+    big = torch.empty(4 * 2048 + 8, dtype=torch.bfloat16, device="cuda")
+    shifted = big[1:1 + 4 * 2048].view(4, 2048)
+    with pytest.raises(mfr.MFRError) as e:
+        mfr.moe_finalize_rmsnorm(*args, d["eps"], d["scale"], residual_out=shifted)
+    assert e.value.status == 3  # MFR_ERR_ALIGN
+    # outputs overlapping an input
+    with pytest.raises(mfr.MFRError) as e:
+        mfr.moe_finalize_rmsnorm(*args, d["eps"], d["scale"], normed_out=dd["shared_out"])
+    assert e.value.status == 4  # MFR_ERR_ALIAS
+    # wrong dtype / layout / device are refused by the binding itself
+    with pytest.raises(TypeError):
+        mfr.moe_finalize_rmsnorm(args[0].float(), *args[1:], d["eps"], d["scale"])
+    strided = torch.empty(2048, 4, dtype=torch.bfloat16, device="cuda").t()  # [4, 2048], not contiguous
+    with pytest.raises(ValueError):
+        mfr.moe_finalize_rmsnorm(*args[:3], strided, *args[4:], d["eps"], d["scale"])
+    with pytest.raises(ValueError):
+        mfr.moe_finalize_rmsnorm(*args, d["eps"], d["scale"],
+                                 residual_out=torch.empty(4, 2048, dtype=torch.bfloat16))
+    # a masked-everything call with NaN weights still works (weights of masked slots ignored)
+    p = torch.full_like(dd["perm_idx"], -1)
+    w = torch.full_like(dd["topk_w"], float("nan"))
+    r, n = mfr.moe_finalize_rmsnorm(args[0], p, w, *args[3:], d["eps"], d["scale"])
+    torch.cuda.synchronize()
+    assert not torch.isnan(r.float()).any() and not torch.isnan(n.float()).any()
+
+
+def test_zero_tokens_every_entry_point():
+    d = synth.generate(0, 2048, 8, seed=902)
+    dd = gu.to_device(d)
+    r, q, sc, n = mfr.moe_finalize_rmsnorm_fp8(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
+                                               dd["shared_out"], dd["residual"], dd["gamma"],
+                                               1e-6, 1.0, bf16_normed=True)
+    assert q.shape == (0, 2048) and sc.shape == (0,) and n.shape == (0, 2048)
+    r, n = mfr.residual_add_rmsnorm(dd["shared_out"], dd["residual"], dd["gamma"], 1e-6)
+    assert r.shape == (0, 2048)

@@ -99,6 +99,12 @@ def _check(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _same_device(*tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+
+
 def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
                          residual_out=None, normed_out=None, stream=None):
     """Fused MoE finalize + residual add + RMSNorm on the current (or given) stream.
@@ -131,6 +137,7 @@ def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gam
     _check(normed_out, "normed_out", torch.bfloat16, 2)
     if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
         raise ValueError("outputs must be [T, H]")
+    _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out, normed_out)
     if stream is None:
         stream = torch.cuda.current_stream(residual.device)
     rc = _lib.moe_finalize_rmsnorm(
@@ -168,6 +175,7 @@ def residual_add_rmsnorm(x, residual, gamma, eps, residual_out=None, normed_out=
     _check(normed_out, "normed_out", torch.bfloat16, 2)
     if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
         raise ValueError("outputs must be [T, H]")
+    _same_device(x, residual, gamma, residual_out, normed_out)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     rc = _lib.residual_add_rmsnorm(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
@@ -223,6 +231,8 @@ def moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual,
     _check(fp8_scale, "fp8_scale", torch.float32, 1)
     if normed_out is not None:
         _check(normed_out, "normed_out", torch.bfloat16, 2)
+    _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out,
+                 normed_fp8, fp8_scale, normed_out)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     rc = _lib.moe_finalize_rmsnorm_fp8(
