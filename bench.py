@@ -37,7 +37,7 @@ METRIC = "fused MoE-finalize+RMSNorm µs/call and effective HBM GB/s (% of peak)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FUSED_KERNEL_PREFIX = "mfr_"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_prefill_T8192_traffic.json")
-HEADLINE_CFG, HEADLINE_T = 4, 8192
+HEADLINE_CFG, HEADLINE_T = "prefill", 8192
 
 
 def log(*a):
@@ -231,7 +231,7 @@ def decode_latency():
     import synth
     out = {}
     for T in DECODE_TS:
-        d = synth.config_inputs(1, T)
+        d = synth.config_inputs("decode", T)
         dd = to_device(d)
         call, _ = make_caller(dd, d["eps"], d["scale"])
         out[f"T{T}"] = round(time_graph([call], 100, 5) * 1e3, 2)
@@ -242,7 +242,7 @@ def graph_ceiling_batch():
     """The 512-token batch (H=6144, K=8): HBM-cold (a graph cycling over 8
     buffer sets, 604 MB > Infinity Cache) and cache-warm (one set)."""
     import synth
-    d = synth.config_inputs(3, 512)
+    d = synth.config_inputs("batch512", 512)
     nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     sets = [to_device(d) for _ in range(8)]
     calls = [make_caller(dd, d["eps"], d["scale"])[0] for dd in sets]
@@ -281,12 +281,12 @@ def dense_figures():
     inside a graph."""
     import synth
     T, H = 8192, 6144
-    d = synth.dense_inputs(T, H, seed=synth.seed_for(4, T), spike_frac=0.01)
+    d = synth.dense_inputs(T, H, seed=synth.seed_for("prefill", T), spike_frac=0.01)
     nbytes = synth.dense_algorithmic_bytes(T, H)
     calls = [make_dense_caller(d) for _ in range(3)]
     ms = time_calls(calls, 60, 6)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    small = synth.dense_inputs(28, H, seed=synth.seed_for(1, 28))
+    small = synth.dense_inputs(28, H, seed=synth.seed_for("decode", 28))
     dec = time_graph([make_dense_caller(small)], 100, 5) * 1e3
     return {"prefill_T8192": {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
                               "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes},
@@ -318,11 +318,11 @@ def fp8_figures():
                 raise RuntimeError(mfr.strerror(rc))
         call.keep = (dd, ro, q, sc)
         return call
-    d = synth.config_inputs(4, 8192)
+    d = synth.config_inputs("prefill", 8192)
     nbytes = synth.fp8_algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     ms = time_calls([caller(d)], 60, 6)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    dec = time_graph([caller(synth.config_inputs(1, 28))], 100, 5) * 1e3
+    dec = time_graph([caller(synth.config_inputs("decode", 28))], 100, 5) * 1e3
     return {"prefill_T8192": {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
                               "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes},
             "decode_T28_us": round(dec, 2)}
@@ -335,7 +335,7 @@ def deferred_overhead():
     import torch
     import synth
     import top_finalize_residual_amd as mfr
-    d = synth.config_inputs(1, 28)
+    d = synth.config_inputs("decode", 28)
     dd = to_device(d)
     u = mfr.UnfinalizedMoEOutput(dd["expert_out"], dd["perm_idx"], dd["topk_w"], d["scale"])
     mo = mfr.MoEOutput(u, dd["shared_out"])
@@ -355,7 +355,7 @@ def run_latency(args):
     import torch
     import synth
     torch.cuda.set_device(0)
-    for cfg, T in [(1, t) for t in DECODE_TS] + [(3, 512)]:
+    for cfg, T in [("decode", t) for t in DECODE_TS] + [("batch512", 512)]:
         d = synth.config_inputs(cfg, T)
         dd = to_device(d)
         call, _ = make_caller(dd, d["eps"], d["scale"])
@@ -364,7 +364,7 @@ def run_latency(args):
         torch.cuda.synchronize()
         log(f"T={T}: {args.steps} calls")
     for T in (28, 8192):
-        call = make_dense_caller(synth.dense_inputs(T, 6144, seed=synth.seed_for(4, T)))
+        call = make_dense_caller(synth.dense_inputs(T, 6144, seed=synth.seed_for("prefill", T)))
         for _ in range(args.steps if T < 8192 else 20):
             call()
         torch.cuda.synchronize()
@@ -461,7 +461,7 @@ def summarize_trace(args):
         key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = [f"# rocprofv3 kernel trace: {args.title}", "",
-             "Commands ($REPO is the repository root; the GPU run writes gpurun_out/):", "",
+             "Commands ($REPO is the repository root, $OUT any output directory):", "",
              "```", args.command, "```", "",
              "| kernel | grid (threads) | workgroup | tokens | calls | avg µs | median µs | min µs | max µs |",
              "|---|---|---|---|---|---|---|---|---|"]

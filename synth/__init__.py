@@ -16,7 +16,8 @@ Workloads (shapes from the pages, distributions chosen for this library):
     ("vLLM pull request #62174", Validation: tokens 1, 4, 64 and hidden
     2048/6144 in its fused all-reduce RMSNorm test).
 
-Generator: numpy PCG64 with seed = 20261202 + 1000*cfg + T; SeedSequence(seed)
+Generator: numpy PCG64 with seed = 20261202 + 1000*seed_index + T (each named
+workload has a seed index); SeedSequence(seed)
 spawns one child stream per tensor, in the order expert_out, perm, logits,
 shared, residual, gamma, mask, spikes. Normals are drawn in float32, scaled as
 mu + sigma*z in float32, then rounded to bf16 (round-to-nearest-even).
@@ -29,25 +30,31 @@ import torch
 BASE_SEED = 20261202
 STREAMS = ("expert_out", "perm", "logits", "shared", "residual", "gamma", "mask", "spikes")
 
-# Config recipes. Ts lists the token counts each config is run at.
+# Workload recipes, by name. Ts lists the token counts each is run at; seed_index
+# enters the seed (seed = 20261202 + 1000 * seed_index + T).
 CONFIGS = {
-    0: dict(Ts=(4,), H=2048, K=8, scale=1.0, weights="softmax_k", mask_frac=0.0, spike_frac=0.0,
-            name="tiny: T=4 H=2048 K=8"),
-    1: dict(Ts=(1, 4, 12, 28, 64), H=6144, K=8, scale=2.5, weights="softmax_k", mask_frac=0.0,
-            spike_frac=0.0, name="decode latency sweep: H=6144 K=8"),
-    2: dict(Ts=(1, 4, 64), H=2048, K=8, scale=2.5, weights="softmax_k", mask_frac=0.05,
-            spike_frac=0.0, name="small-hidden decode, 5% masked slots: H=2048 K=8"),
-    3: dict(Ts=(512,), H=6144, K=8, scale=2.5, weights="top8_of_256", mask_frac=0.0,
-            spike_frac=0.0, name="batched decode at graph ceiling: T=512 H=6144 K=8"),
-    4: dict(Ts=(8192,), H=6144, K=8, scale=2.5, weights="top8_of_256", mask_frac=0.0,
-            spike_frac=0.01, name="prefill chunk: T=8192 H=6144 K=8, 1% residual rows x100"),
+    "tiny": dict(seed_index=0, Ts=(4,), H=2048, K=8, scale=1.0, weights="softmax_k",
+                 mask_frac=0.0, spike_frac=0.0, name="tiny: T=4 H=2048 K=8"),
+    "decode": dict(seed_index=1, Ts=(1, 4, 12, 28, 64), H=6144, K=8, scale=2.5,
+                   weights="softmax_k", mask_frac=0.0, spike_frac=0.0,
+                   name="decode latency sweep: H=6144 K=8"),
+    "decode_masked": dict(seed_index=2, Ts=(1, 4, 64), H=2048, K=8, scale=2.5, weights="softmax_k",
+                          mask_frac=0.05, spike_frac=0.0,
+                          name="small-hidden decode, 5% masked slots: H=2048 K=8"),
+    "batch512": dict(seed_index=3, Ts=(512,), H=6144, K=8, scale=2.5, weights="top8_of_256",
+                     mask_frac=0.0, spike_frac=0.0,
+                     name="batched decode at graph ceiling: T=512 H=6144 K=8"),
+    "prefill": dict(seed_index=4, Ts=(8192,), H=6144, K=8, scale=2.5, weights="top8_of_256",
+                    mask_frac=0.0, spike_frac=0.01,
+                    name="prefill chunk: T=8192 H=6144 K=8, 1% residual rows x100"),
 }
 EPS = 1e-6
 _CHUNK = 1 << 22  # values per float32 chunk when drawing large tensors
 
 
 def seed_for(cfg, T):
-    return BASE_SEED + 1000 * cfg + T
+    """Seed of a named workload at token count T."""
+    return BASE_SEED + 1000 * CONFIGS[cfg]["seed_index"] + T
 
 
 def f32_to_bf16_bits(x):

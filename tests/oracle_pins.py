@@ -201,7 +201,7 @@ def _csr_weights(perm, w, R):
 def pin_sparse_matmul(o):
     """Library special case: the routed part equals scale * (W @ E) with W the
     sparse [T, R] matrix of routing weights (scipy.sparse, fp64)."""
-    for cfg, T in ((0, 4), (2, 64), (2, 1)):
+    for cfg, T in (("tiny", 4), ("decode_masked", 64), ("decode_masked", 1)):
         d = synth.config_inputs(cfg, T)
         out = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                                  d["residual"], d["gamma"], d["eps"], d["scale"])
@@ -216,7 +216,7 @@ def pin_sparse_matmul(o):
 def pin_rms_norm_library(o):
     """Library special case: torch.nn.functional.rms_norm in float64 on the
     oracle's unrounded sum reproduces its unrounded normed value."""
-    for cfg, T in ((0, 4), (2, 64), (1, 4)):
+    for cfg, T in (("tiny", 4), ("decode_masked", 64), ("decode", 4)):
         d = synth.config_inputs(cfg, T)
         out = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                                  d["residual"], d["gamma"], d["eps"], d["scale"])
@@ -249,7 +249,7 @@ def pin_slot_permutation(o):
     """Permuting the K slots of a token (index and weight together) leaves the
     outputs unchanged."""
     rng = np.random.default_rng(5)
-    for cfg, T in ((0, 4), (2, 64)):
+    for cfg, T in (("tiny", 4), ("decode_masked", 64)):
         d = synth.config_inputs(cfg, T)
         base = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                                   d["residual"], d["gamma"], d["eps"], d["scale"])
@@ -283,7 +283,7 @@ def pin_zero_routed(o):
 def pin_scale_invariance(o):
     """shared, residual and scale times c = 2^j, eps times c^2: residual_out
     scales by exactly c and normed_out is unchanged."""
-    d = synth.config_inputs(0, 4)
+    d = synth.config_inputs("tiny", 4)
     base = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                               d["residual"], d["gamma"], d["eps"], d["scale"])
     for j in (-2, 3):
@@ -299,7 +299,7 @@ def pin_scale_invariance(o):
 
 def pin_unit_rms(o):
     """gamma = 1: the RMS of each token's normed output is sqrt(ms / (ms + eps))."""
-    d = synth.config_inputs(1, 4)
+    d = synth.config_inputs("decode", 4)
     ones = synth.f32_to_bf16_bits(np.ones(d["H"], dtype=np.float32))
     out = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                              d["residual"], ones, d["eps"], d["scale"])
@@ -314,7 +314,7 @@ def pin_unit_rms(o):
 def pin_masked_nan_poison(o):
     """Masked slots are skipped entirely: NaN weights on masked slots and NaN in
     every row that no valid index names leave the outputs bit-identical."""
-    d = synth.config_inputs(2, 64)
+    d = synth.config_inputs("decode_masked", 64)
     base = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                               d["residual"], d["gamma"], d["eps"], d["scale"])
     E = d["expert_out"].copy()
@@ -494,7 +494,7 @@ def pin_fp8_quantize_properties(o):
     exactly +-448; every code is the nearest E4M3 value of y / scale; powers of
     two of y leave the codes unchanged and scale the scale; an all-zero row has
     scale 1 and zero codes."""
-    d = synth.config_inputs(1, 12)
+    d = synth.config_inputs("decode", 12)
     y = o.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
                            d["residual"], d["gamma"], d["eps"], d["scale"])["normed_exact"]
     codes, scales, scaled = o.fp8_quantize_rows(y)

@@ -51,7 +51,7 @@ def test_dense_parity(T, H, path):
 
 
 def test_dense_prefill_full_size_sampled():
-    d = synth.dense_inputs(8192, 6144, seed=synth.seed_for(4, 8192), spike_frac=0.01)
+    d = synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192), spike_frac=0.01)
     r, n = run_dense(d)
     rng = np.random.default_rng(3)
     tokens = np.sort(np.concatenate([d["spike_rows"], rng.choice(8192, 200, replace=False)]))

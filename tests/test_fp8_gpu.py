@@ -66,11 +66,12 @@ def check_fp8(codes, scales, ref, gamma, eps):
     return want
 
 
-CASES = [(0, 4), (1, 1), (1, 28), (1, 64), (2, 64), (3, 512)]
+CASES = [("tiny", 4), ("decode", 1), ("decode", 28), ("decode", 64), ("decode_masked", 64),
+         ("batch512", 512)]
 
 
 @pytest.mark.parametrize("path", [0, mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["auto", "token", "stream"])
-@pytest.mark.parametrize("cfg,T", CASES, ids=[f"cfg{c}-T{t}" for c, t in CASES])
+@pytest.mark.parametrize("cfg,T", CASES, ids=[f"{c}-T{t}" for c, t in CASES])
 def test_fp8_parity(cfg, T, path):
     d = synth.config_inputs(cfg, T)
     dd = gu.to_device(d)
@@ -83,7 +84,7 @@ def test_fp8_parity(cfg, T, path):
 
 
 def test_fp8_without_bf16_normed_and_store_policies():
-    d = synth.config_inputs(3, 512)
+    d = synth.config_inputs("batch512", 512)
     dd = gu.to_device(d)
     r1, q1, s1, n1 = run_fp8(dd, d)
     assert n1 is None
@@ -94,7 +95,7 @@ def test_fp8_without_bf16_normed_and_store_policies():
 
 
 def test_fp8_prefill_full_size_sampled():
-    d = synth.config_inputs(4, 8192)
+    d = synth.config_inputs("prefill", 8192)
     dd = gu.to_device(d)
     r, q, sc, _ = run_fp8(dd, d)
     rng = np.random.default_rng(7)

@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 PATHS = [0, mfr.PATH_TOKEN, mfr.PATH_STREAM]
 PATH_IDS = ["auto", "token", "stream"]
 
-CONFIG_CASES = [(cfg, T) for cfg in (0, 1, 2, 3) for T in synth.CONFIGS[cfg]["Ts"]]
+CONFIG_CASES = [(cfg, T) for cfg in ("tiny", "decode", "decode_masked", "batch512")
+                for T in synth.CONFIGS[cfg]["Ts"]]
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +31,7 @@ def cfg_data():
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
-@pytest.mark.parametrize("cfg,T", CONFIG_CASES, ids=[f"cfg{c}-T{t}" for c, t in CONFIG_CASES])
+@pytest.mark.parametrize("cfg,T", CONFIG_CASES, ids=[f"{c}-T{t}" for c, t in CONFIG_CASES])
 def test_config_parity(cfg_data, cfg, T, path):
     d, dd, ref = cfg_data(cfg, T)
     r, n = gu.run(dd, d["eps"], d["scale"], path=path)
@@ -39,7 +40,7 @@ def test_config_parity(cfg_data, cfg, T, path):
 
 @pytest.mark.parametrize("vpt", [1, 2, 3, 4])
 @pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
-@pytest.mark.parametrize("cfg,T", [(0, 4), (1, 28), (2, 64)])
+@pytest.mark.parametrize("cfg,T", [("tiny", 4), ("decode", 28), ("decode_masked", 64)])
 def test_tile_variants(cfg_data, cfg, T, path, vpt):
     d, dd, ref = cfg_data(cfg, T)
     r, n = gu.run(dd, d["eps"], d["scale"], path=path, vpt=vpt)
@@ -50,7 +51,7 @@ def test_tile_variants(cfg_data, cfg, T, path, vpt):
                          ids=["write_back", "write_through"])
 @pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
 def test_store_policies(cfg_data, path, store):
-    d, dd, ref = cfg_data(3, 512)
+    d, dd, ref = cfg_data("batch512", 512)
     r, n = gu.run(dd, d["eps"], d["scale"], path=path, store=store)
     gu.check(d, r, n, ref=ref)
 
@@ -59,7 +60,7 @@ def test_prefill_chunk_full_size_sampled():
     """The 8192-token prefill chunk at full size in the default (benchmarked)
     launch configuration; the oracle checks every spiked row plus a seeded
     sample of the others."""
-    d = synth.config_inputs(4, 8192)
+    d = synth.config_inputs("prefill", 8192)
     assert mfr.moe_finalize_rmsnorm_path(8192, d["H"], d["K"]) == mfr.PATH_STREAM
     dd = gu.to_device(d)
     r, n = gu.run(dd, d["eps"], d["scale"])
@@ -97,7 +98,7 @@ def test_zero_tokens():
 def test_masked_slots_never_read(path):
     """NaN in every row no valid index names, and NaN weights on masked slots:
     outputs bit-identical to the clean run."""
-    d = synth.config_inputs(2, 64)
+    d = synth.config_inputs("decode_masked", 64)
     dd = gu.to_device(d)
     r0, n0 = gu.run(dd, d["eps"], d["scale"], path=path)
     E = d["expert_out"].copy()
@@ -114,7 +115,7 @@ def test_masked_slots_never_read(path):
 @pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
 def test_masked_slot_position_is_irrelevant(path):
     """Moving a token's masked slots to the end leaves its outputs bit-identical."""
-    d = synth.config_inputs(2, 64)
+    d = synth.config_inputs("decode_masked", 64)
     dd = gu.to_device(d)
     r0, n0 = gu.run(dd, d["eps"], d["scale"], path=path)
     p, w = d["perm_idx"].copy(), d["topk_w"].copy()
@@ -150,7 +151,7 @@ def test_no_routed_contribution(path, variant):
 def test_permutation_handling_bitexact(path):
     """Gathering through a permutation equals, bit for bit, reading rows that
     were pre-permuted on the host through the identity map."""
-    d = synth.config_inputs(1, 64)
+    d = synth.config_inputs("decode", 64)
     dd = gu.to_device(d)
     r0, n0 = gu.run(dd, d["eps"], d["scale"], path=path)
     T, K = d["perm_idx"].shape
@@ -162,7 +163,7 @@ def test_permutation_handling_bitexact(path):
 
 
 def test_deterministic_and_path_independent():
-    d = synth.config_inputs(3, 512)
+    d = synth.config_inputs("batch512", 512)
     dd = gu.to_device(d)
     ra, na = gu.run(dd, d["eps"], d["scale"], path=mfr.PATH_STREAM)
     rb, nb = gu.run(dd, d["eps"], d["scale"], path=mfr.PATH_STREAM)
@@ -183,7 +184,7 @@ def test_deterministic_and_path_independent():
 
 def test_batch_invariance():
     """A token's outputs do not depend on the other tokens in the call."""
-    d = synth.config_inputs(1, 64)
+    d = synth.config_inputs("decode", 64)
     dd = gu.to_device(d)
     r, n = gu.run(dd, d["eps"], d["scale"], path=mfr.PATH_TOKEN)
     for t in (0, 17, 63):
@@ -195,7 +196,7 @@ def test_batch_invariance():
 
 @pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
 def test_in_place_residual(path):
-    d = synth.config_inputs(1, 28)
+    d = synth.config_inputs("decode", 28)
     dd = gu.to_device(d)
     r0, n0 = gu.run(dd, d["eps"], d["scale"], path=path)
     resid = dd["residual"].clone()
@@ -208,7 +209,7 @@ def test_in_place_residual(path):
 def test_graph_capture_replay():
     """Calls captured into a HIP graph (through torch) replay correctly, again
     and again, with eager work and synchronisations between replays."""
-    d = synth.config_inputs(1, 28)
+    d = synth.config_inputs("decode", 28)
     dd = gu.to_device(d)
     r_eager, n_eager = gu.run(dd, d["eps"], d["scale"])
     r_out = torch.empty_like(dd["residual"])
