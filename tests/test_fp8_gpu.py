@@ -7,7 +7,8 @@ same 1e-6 absolute floor the bf16 gate allows, carried through the
 normalisation and the scale) plus a relative 2^-18. Where the exact y / scale
 lies that close to the midpoint between two E4M3 neighbours, either is a
 correct rounding and the GPU's code may be the other one. Scales agree to
-fp32 accuracy."""
+fp32 accuracy: a relative 2^-20, plus the spacing 2^-149 of fp32 subnormals
+for the scale of a row whose largest value is tiny."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +21,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 SCALE_REL = 2.0 ** -20
+SCALE_ABS = 2.0 ** -149  # spacing of fp32 subnormals
 TIE_REL = 2.0 ** -18
 
 
@@ -49,7 +51,7 @@ def check_fp8(codes, scales, ref, gamma, eps):
     """ref: the oracle's finalize outputs (s, normed_exact) for these rows."""
     normed_exact = ref["normed_exact"]
     want, want_scale, scaled = oracle.fp8_quantize_rows(normed_exact)
-    assert np.all(np.abs(scales - want_scale) <= SCALE_REL * want_scale), "scale"
+    assert np.all(np.abs(scales - want_scale) <= SCALE_REL * want_scale + SCALE_ABS), "scale"
     diff = np.abs(e4m3_key(codes) - e4m3_key(want))
     assert diff.max(initial=0) <= 1, f"codes {int(diff.max())} steps apart"
     if diff.any():
@@ -126,3 +128,52 @@ def test_fp8_zero_row():
     r, q, sc, _ = run_fp8(dd, d)
     assert sc[1] == 1.0 and np.all(e4m3_key(q[1]) == 0)
     check_fp8(q, sc, gu.oracle_for(d), d["gamma"], d["eps"])
+
+
+def test_fp8_tiny_row():
+    """A token whose sum is made of bf16 subnormals no larger than 7 * 2^-133
+    (shared and routed parts zero, eps 1e-4): its amax lies far below
+    448 / FLT_MAX, so 448 / amax overflows fp32. Every code still matches the
+    oracle (this row's sum is exact, so a code may differ only at a tie, to
+    fp32 rounding of the scaled value), zeros stay zero and no NaN code
+    appears."""
+    T, H, t = 4, 2048, 2
+    d = synth.generate(T, H, 8, scale=1.0, seed=72)
+    d["eps"] = float(np.float32(1e-4))
+    d["topk_w"][t] = 0.0
+    d["shared_out"][t] = 0
+    rng = np.random.default_rng(3)
+    mant = rng.integers(0, 8, size=H).astype(np.uint16)
+    sign = rng.integers(0, 2, size=H).astype(np.uint16) << np.uint16(15)
+    d["residual"][t] = sign | mant
+    dd = gu.to_device(d)
+    r, q, sc, _ = run_fp8(dd, d)
+    ref = gu.oracle_for(d)
+    want, want_scale, scaled = oracle.fp8_quantize_rows(ref["normed_exact"])
+    amax = want_scale[t] * 448.0
+    assert 448.0 / amax > np.finfo(np.float32).max  # the case under test
+    check_fp8(q, sc, ref, d["gamma"], d["eps"])
+    diff = np.abs(e4m3_key(q[t]) - e4m3_key(want[t]))
+    assert diff.max() <= 1
+    i = np.nonzero(diff)[0]
+    mid = (e4m3_values(q[t][i]) + e4m3_values(want[t][i])) / 2
+    assert np.all(np.abs(scaled[t][i] - mid) <= TIE_REL * np.abs(scaled[t][i]))
+    zero = (d["residual"][t] & 0x7FFF) == 0
+    assert zero.any() and np.all(e4m3_key(q[t][zero]) == 0)
+
+
+def test_fp8_nan_gamma_element():
+    """A NaN in gamma makes that column of y NaN: its codes are the NaN code;
+    amax is taken over the other values (as the oracle takes it), so every
+    other code and the scales match the oracle."""
+    T, H, col = 8, 2048, 100
+    d = synth.generate(T, H, 8, scale=2.5, seed=73)
+    d["gamma"] = d["gamma"].copy()
+    d["gamma"][col] = 0x7FC0
+    dd = gu.to_device(d)
+    r, q, sc, _ = run_fp8(dd, d)
+    ref = gu.oracle_for(d)
+    assert np.all((q[:, col] & 0x7F) == 0x7F)
+    keep = np.arange(H) != col
+    sub = dict(s=ref["s"][:, keep], normed_exact=ref["normed_exact"][:, keep])
+    check_fp8(q[:, keep], sc, sub, d["gamma"][keep], d["eps"])

@@ -75,12 +75,26 @@ __device__ __forceinline__ void buf_store_b32(float v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, AUX);
 }
 
-// Clamp to the finite OCP E4M3 range [-448, 448] before the hardware
-// conversion, keeping NaN as NaN (the conversion would otherwise turn values
-// just above 448 into NaN).
-__device__ __forceinline__ float sat_e4m3(float v) {
-    const float c = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
-    return v != v ? v : c;
+// 448 / m for m > 0, made safe to scale by: the correctly rounded quotient,
+// lowered by one ulp where m times it rounds above 448. Rounding is monotone,
+// so |x| <= m then gives |x * factor| <= 448 after rounding, the largest
+// finite OCP E4M3 magnitude (the hardware conversion turns values above it
+// into NaN). m = +inf gives 0.
+__device__ __forceinline__ float e4m3_factor(float m) {
+    float f = 448.0f / m;
+    if (m * f > 448.0f) f = __uint_as_float(__float_as_uint(f) - 1u);
+    return f;
+}
+
+// Eight fp32 values in [-448, 448] (or NaN) to eight OCP E4M3 codes in
+// element order, through the CDNA4 packed conversion v_cvt_pk_fp8_f32, which
+// rounds to nearest-even and maps NaN to the NaN code.
+__device__ __forceinline__ u32x2 pack_e4m3x8(const float (&v)[8]) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+    return u32x2{static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
 }
 
 // One DPP move of a float within a row of 16 lanes (every lane active).

@@ -182,10 +182,12 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     }
 
     // s = (routed + shared) + residual (dense: x + residual); residual_out =
-    // bf16(s); per-lane sum of squares, and (FP8 modes) per-lane max |s * gamma|.
+    // bf16(s); per-lane sum of squares, and (FP8 modes) sg = s * gamma with its
+    // per-lane max |sg|.
     const rsrc_t ro_r = make_rsrc(p.residual_out + trow, rowbytes);
     float ss = 0.0f;
     float mg = 0.0f;
+    float sg[VPT][8];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
 #pragma unroll
@@ -195,8 +197,10 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
             else
                 acc[j][e] = (acc[j][e] + vec_elem(sh[j], e)) + vec_elem(rs[j], e);
             ss = __builtin_fmaf(acc[j][e], acc[j][e], ss);
-            if (QM != kOutBf16)
-                mg = __builtin_fmaxf(mg, __builtin_fabsf(acc[j][e] * vec_elem(gm[j], e)));
+            if (QM != kOutBf16) {
+                sg[j][e] = acc[j][e] * vec_elem(gm[j], e);
+                mg = __builtin_fmaxf(mg, __builtin_fabsf(sg[j][e]));
+            }
         }
         u32x4 o;
         o.x = pack_bf16x2(acc[j][0], acc[j][1]);
@@ -209,61 +213,90 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     // Row reduction: wave tree, then the waves' partial sums in order. The FP8
     // modes reduce max |s * gamma| alongside, through the same exchange and
     // barrier: since rstd > 0, max |y| = rstd * max |s * gamma|.
+    // The slots of waves the workgroup does not have are set to +0 before the
+    // barrier, so that afterwards every thread reads all MAX_WAVES slots at
+    // once (one LDS round trip, no loop) and folds them in wave order. Every
+    // partial is +0 or more (or NaN), so adding the +0 slots and taking their
+    // max changes neither result.
     const float wsum = wave_sum(ss);
     const float wmg = QM != kOutBf16 ? wave_max(mg) : 0.0f;
+    const int nw = nt >> 6;
     if ((tid & 63) == 0) {
         red[tid >> 6] = wsum;
         if (QM != kOutBf16) red[MAX_WAVES + (tid >> 6)] = wmg;
     }
+    if (tid >= nw && tid < MAX_WAVES) {
+        red[tid] = 0.0f;
+        if (QM != kOutBf16) red[MAX_WAVES + tid] = 0.0f;
+    }
     __syncthreads();
+    constexpr int NRED = QM != kOutBf16 ? 2 * MAX_WAVES : MAX_WAVES;
+    float part[NRED];
+#pragma unroll
+    for (int w = 0; w < NRED; ++w) part[w] = red[w];
+    __builtin_amdgcn_sched_barrier(0);  // all slot reads in flight before the first use
     float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < MAX_WAVES; ++w) tot += part[w];
     float rmg = 0.0f;
-    const int nw = nt >> 6;
-    for (int w = 0; w < nw; ++w) tot += red[w];
-    if (QM != kOutBf16)
-        for (int w = 0; w < nw; ++w) rmg = __builtin_fmaxf(rmg, red[MAX_WAVES + w]);
+#pragma unroll
+    for (int w = MAX_WAVES; w < NRED; ++w) rmg = __builtin_fmaxf(rmg, part[w]);
     const float rstd = 1.0f / __builtin_sqrtf(tot / p.h_f + p.eps);
-
-    float y[VPT][8];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[j][e] = (acc[j][e] * rstd) * vec_elem(gm[j], e);
 
     if (QM != kOutFp8) {
         const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (acc[j][e] * rstd) * vec_elem(gm[j], e);
             u32x4 o;
-            o.x = pack_bf16x2(y[j][0], y[j][1]);
-            o.y = pack_bf16x2(y[j][2], y[j][3]);
-            o.z = pack_bf16x2(y[j][4], y[j][5]);
-            o.w = pack_bf16x2(y[j][6], y[j][7]);
+            o.x = pack_bf16x2(y[0], y[1]);
+            o.y = pack_bf16x2(y[2], y[3]);
+            o.z = pack_bf16x2(y[4], y[5]);
+            o.w = pack_bf16x2(y[6], y[7]);
             buf_store<OUT_AUX>(o, no_r, off[j]);
         }
     }
 
     if (QM != kOutBf16) {
-        // Dynamic per-token FP8: amax = max |y| = rstd * max |s * gamma|,
-        // scale = amax / 448, codes = E4M3(y * 448 / amax), saturated (the
-        // fp32 product can overshoot 448 by an ulp).
+        // Dynamic per-token FP8: amax = max |y| = rstd * max |sg|, scale =
+        // amax / 448, codes = E4M3(y * 448 / amax). Since rstd > 0 is common
+        // to y and amax, y * 448 / amax = sg * (448 / max |sg|): one multiply
+        // per element, with no rstd in it.
+        //   * The factor is rounded down by an ulp where max |sg| times it
+        //     exceeds 448, so (rounding being monotone) no element can pass
+        //     448 and the conversion needs no clamp.
+        //   * Rows with max |sg| < 2^-100, where 448 / max |sg| could
+        //     overflow, are scaled by 2^64 first (exact).
+        //   * A row with amax = 0, or rstd NaN, 0 or infinite, keeps the
+        //     direct form y * 0: codes 0, or NaN where y is NaN; scale 1.
+        // NaN elements (a NaN gamma) stay NaN; the conversion maps them to
+        // the NaN code.
         const float rmax = rmg * rstd;
         const bool zero_row = !(rmax > 0.0f);
         const float qscale = zero_row ? 1.0f : rmax / kE4m3Max;
-        const float inv = zero_row ? 0.0f : kE4m3Max / rmax;
         const rsrc_t q_r = make_rsrc(p.normed_fp8 + t * static_cast<int64_t>(p.V) * 8,
                                      static_cast<uint32_t>(p.V) * 8u);
+        if (!zero_row && rmg >= 0x1p-100f) {
+            const float f = e4m3_factor(rmg);
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            float v[8];
+            for (int j = 0; j < VPT; ++j) {
+                float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = sat_e4m3(y[j][e] * inv);
-            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-            lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
-            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-            hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
-            u32x2 q = {static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
-            buf_store_b64<OUT_AUX>(q, q_r, off[j] >> 1);  // 8 code bytes per 16 bf16 bytes
+                for (int e = 0; e < 8; ++e) v[e] = sg[j][e] * f;
+                buf_store_b64<OUT_AUX>(pack_e4m3x8(v), q_r, off[j] >> 1);
+            }
+        } else {
+            const float a = zero_row ? rstd : 0x1p64f;
+            const float b = zero_row ? 0.0f : e4m3_factor(rmg * 0x1p64f);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (sg[j][e] * a) * b;
+                buf_store_b64<OUT_AUX>(pack_e4m3x8(v), q_r, off[j] >> 1);
+            }
         }
         if (tid == 0) {
             const rsrc_t s_r = make_rsrc(p.fp8_scale + t, 4u);
@@ -284,7 +317,8 @@ struct Bound {
 // OutMode of the normalised output.
 template <int VPT, int KT, int OUT_AUX, int QM>
 __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(Params p) {
-    __shared__ float red[2 * MAX_WAVES];  // per-wave row sums and (FP8 modes) row maxima
+    // Per-wave row sums and (FP8 modes) row maxima; 16-byte aligned for vector reads.
+    __shared__ __align__(16) float red[2 * MAX_WAVES];
     finalize_token<VPT, KT, OUT_AUX, QM>(p, static_cast<int64_t>(blockIdx.x), red);
 }
 
