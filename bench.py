@@ -142,16 +142,22 @@ def _probe_lib():
     import ctypes
     from top_finalize_residual_amd import build as b
     lib = ctypes.CDLL(b.PROBE_LIB)
-    for fn in (lib.mfr_copy_probe, lib.mfr_read_probe):
+    for fn in (lib.mfr_copy_probe, lib.mfr_read_probe, lib.mfr_touch_probe):
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                        ctypes.c_void_p]
+    lib.mfr_write_probe.restype = ctypes.c_int
+    lib.mfr_write_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.mfr_empty_probe.restype = ctypes.c_int
+    lib.mfr_empty_probe.argtypes = [ctypes.c_void_p]
     return lib
 
 
 def probe_ceilings(nbytes=1 << 30, reps=10):
-    """GB/s of the copy probe (read + write bytes) and of the read-only probe,
-    on 1 GiB buffers (4x the Infinity Cache, so both stream from HBM)."""
+    """GB/s of the copy probe (read + write bytes), the read-only probe and
+    the write-only probe, on 1 GiB buffers (4x the Infinity Cache, so all
+    three stream from HBM)."""
     import torch
     lib = _probe_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -170,11 +176,28 @@ def probe_ceilings(nbytes=1 << 30, reps=10):
         if lib.mfr_read_probe(src.data_ptr(), sink.data_ptr(), nbytes, grid,
                               torch.cuda.current_stream().cuda_stream) != 0:
             raise RuntimeError("read probe failed")
+    def write():
+        if lib.mfr_write_probe(dst.data_ptr(), nbytes, 0x3F803F80, grid,
+                               torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("write probe failed")
     copy_gbs = 2 * nbytes / (time_calls([copy], reps, 2) * 1e-3) / 1e9
     read_gbs = nbytes / (time_calls([read], reps, 2) * 1e-3) / 1e9
+    write_gbs = nbytes / (time_calls([write], reps, 2) * 1e-3) / 1e9
     del src, dst, sink
     torch.cuda.empty_cache()
-    return copy_gbs, read_gbs
+    return copy_gbs, read_gbs, write_gbs
+
+
+def launch_floor_us():
+    """Per-launch device µs of an empty kernel inside a graph of 100 launches:
+    the floor under any kernel measured the way decode_latency measures."""
+    import torch
+    lib = _probe_lib()
+
+    def empty():
+        if lib.mfr_empty_probe(torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("empty probe failed")
+    return round(time_graph([empty], 100, 5) * 1e3, 2)
 
 
 # ---------------------------------------------------------------------------
@@ -224,18 +247,114 @@ def traffic_for_headline():
 DECODE_TS = (1, 4, 12, 28, 64)
 
 
-def decode_latency():
-    """Per-call device µs at the decode sizes (H=6144, K=8), inside a graph of
-    100 back-to-back calls on one buffer set (the inputs stay in the Infinity
-    Cache, as right after GEMM2 wrote them). Context figures."""
+def _raise_on(rc):
+    if rc != 0:
+        import top_finalize_residual_amd as mfr
+        raise RuntimeError(mfr.strerror(rc))
+
+
+def stacked_calls(d, n, mode="bf16"):
+    """n distinct device copies of one input set, each with its own outputs,
+    and one zero-allocation closure per copy. mode: "bf16" (the fused op),
+    "fp8" (the fused op with only the FP8 normed output) or "dense" (the
+    residual add + RMSNorm, with shared_out as its x)."""
+    import torch
+    import top_finalize_residual_amd as mfr
+    dd = to_device(d)
+    T, K = dd["perm_idx"].shape
+    H = dd["gamma"].shape[0]
+    st = {k: v.unsqueeze(0).repeat((n,) + (1,) * v.dim()) for k, v in dd.items()}
+    ro = torch.empty((n, T, H), dtype=torch.bfloat16, device="cuda")
+    no = torch.empty_like(ro)
+    q = torch.empty((n, T, H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((n, max(T, 1)), dtype=torch.float32, device="cuda")
+    eps, scale = d["eps"], d["scale"]
+    names = ("expert_out", "perm_idx", "topk_w", "shared_out", "residual", "gamma")
+    calls = []
+    for i in range(n):
+        a = [st[k][i].data_ptr() for k in names]
+        r_i, n_i, q_i, s_i = ro[i].data_ptr(), no[i].data_ptr(), q[i].data_ptr(), sc[i].data_ptr()
+        if mode == "bf16":
+            def call(a=a, r_i=r_i, n_i=n_i):
+                _raise_on(mfr.moe_finalize_rmsnorm_raw(*a, eps, scale, r_i, n_i, T, H, K,
+                                                       torch.cuda.current_stream().cuda_stream))
+        elif mode == "fp8":
+            def call(a=a, r_i=r_i, q_i=q_i, s_i=s_i):
+                _raise_on(mfr.moe_finalize_rmsnorm_fp8_raw(*a, eps, scale, r_i, None, q_i, s_i,
+                                                           T, H, K,
+                                                           torch.cuda.current_stream().cuda_stream))
+        elif mode == "dense":
+            def call(a=a, r_i=r_i, n_i=n_i):
+                _raise_on(mfr.residual_add_rmsnorm_raw(a[3], a[4], a[5], eps, r_i, n_i, T, H,
+                                                       torch.cuda.current_stream().cuda_stream))
+        else:
+            raise ValueError(mode)
+        # the closure holds raw addresses: keep every tensor it touches alive
+        call.keep = (st, ro, no, q, sc)
+        calls.append(call)
+    return calls
+
+
+def touch(tensors):
+    """Read every tensor once with ordinary (cache-allocating) loads, so that
+    it is resident in the Infinity Cache afterwards."""
+    import torch
+    lib = _probe_lib()
+    grid = 1024
+    sink = torch.empty(grid, dtype=torch.int32, device="cuda")
+    for t in tensors:
+        nbytes = t.numel() * t.element_size()
+        if nbytes % 16 or t.data_ptr() % 16:
+            raise ValueError("touch needs 16-byte sizes and alignment")
+        if lib.mfr_touch_probe(t.data_ptr(), sink.data_ptr(), nbytes, grid,
+                               torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("touch probe failed")
+    torch.cuda.synchronize()
+
+
+def scrub_infinity_cache(nbytes=512 << 20):
+    """Read twice the 256 MB Infinity Cache of unrelated data with ordinary
+    loads, so that no earlier data stays resident in it."""
+    import torch
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    touch([buf])
+    del buf
+
+
+def decode_latency(cold_bytes=600_000_000):
+    """Per-call device µs at the decode sizes (H=6144, K=8), graph-replayed,
+    with the caches scrubbed first, for two input patterns:
+      * same_inputs: 100 back-to-back calls on one buffer set (its pages stay
+        mapped in the TLBs; the non-temporal row loads keep the data from
+        settling in the caches, so the calls read it from memory);
+      * fresh_inputs: one call on each of n distinct buffer sets (stacked
+        copies, together above cold_bytes, more than twice the Infinity
+        Cache), as a decode step reading rows nothing has touched since they
+        were written.
+    Also the FP8-output and dense variants at T = 28, and the empty-kernel
+    floor. Context figures, not the headline."""
     import synth
-    out = {}
+    same, fresh = {}, {}
+    variants = {}
     for T in DECODE_TS:
         d = synth.config_inputs("decode", T)
-        dd = to_device(d)
-        call, _ = make_caller(dd, d["eps"], d["scale"])
-        out[f"T{T}"] = round(time_graph([call], 100, 5) * 1e3, 2)
-    return out
+        modes = ("bf16", "fp8", "dense") if T == 28 else ("bf16",)
+        nb = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+        n = max(2, -(-cold_bytes // nb))
+        for mode in modes:
+            calls = stacked_calls(d, 1, mode)
+            scrub_infinity_cache()
+            a = round(time_graph(calls, 100, 5) * 1e3, 2)
+            calls = stacked_calls(d, n, mode)
+            scrub_infinity_cache()
+            b = round(time_graph(calls, 1, 3) * 1e3, 2)
+            del calls
+            if mode == "bf16":
+                same[f"T{T}"], fresh[f"T{T}"] = a, b
+            else:
+                variants[f"{mode}_T{T}"] = {"same_inputs": a, "fresh_inputs": b}
+    return {"same_inputs": same, "fresh_inputs": fresh, **variants,
+            "empty_kernel_floor": launch_floor_us()}
 
 
 def graph_ceiling_batch():
@@ -276,9 +395,8 @@ def make_dense_caller(d):
 
 
 def dense_figures():
-    """The dense residual add + RMSNorm (no routed part): the 8192-token chunk
-    HBM-cold (3 rotating buffer sets, 603 MB), and one decode step of 28 tokens
-    inside a graph."""
+    """The dense residual add + RMSNorm (no routed part) on the 8192-token
+    chunk, HBM-cold (3 rotating buffer sets, 603 MB)."""
     import synth
     T, H = 8192, 6144
     d = synth.dense_inputs(T, H, seed=synth.seed_for("prefill", T), spike_frac=0.01)
@@ -286,17 +404,13 @@ def dense_figures():
     calls = [make_dense_caller(d) for _ in range(3)]
     ms = time_calls(calls, 60, 6)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    small = synth.dense_inputs(28, H, seed=synth.seed_for("decode", 28))
-    dec = time_graph([make_dense_caller(small)], 100, 5) * 1e3
     return {"prefill_T8192": {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
-                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes},
-            "decode_T28_us": round(dec, 2)}
+                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}}
 
 
 def fp8_figures():
     """The fused op with its normalised output as per-token FP8 (no bf16 normed
-    output): the 8192-token chunk (HBM-cold by size) and one 28-token decode
-    step inside a graph."""
+    output) on the 8192-token chunk (HBM-cold by size)."""
     import torch
     import synth
     import top_finalize_residual_amd as mfr
@@ -322,10 +436,8 @@ def fp8_figures():
     nbytes = synth.fp8_algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     ms = time_calls([caller(d)], 60, 6)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    dec = time_graph([caller(synth.config_inputs("decode", 28))], 100, 5) * 1e3
     return {"prefill_T8192": {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
-                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes},
-            "decode_T28_us": round(dec, 2)}
+                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}}
 
 
 def deferred_overhead():
@@ -345,8 +457,10 @@ def deferred_overhead():
         mfr.fused_add_rmsnorm(mo, dd["residual"], dd["gamma"], d["eps"], residual_out=ro,
                               normed_out=no)
     raw, _ = make_caller(dd, d["eps"], d["scale"])
-    return {"T": 28, "eager_op_us": round(time_calls([via_op], 300, 30) * 1e3, 2),
-            "eager_raw_us": round(time_calls([raw], 300, 30) * 1e3, 2),
+    eager_op = round(time_calls([via_op], 300, 30) * 1e3, 2)
+    eager_raw = round(time_calls([raw], 300, 30) * 1e3, 2)
+    scrub_infinity_cache()  # the cache state of decode_latency's same_inputs
+    return {"T": 28, "eager_op_us": eager_op, "eager_raw_us": eager_raw,
             "graph_op_us": round(time_graph([via_op], 100, 5) * 1e3, 2)}
 
 
@@ -415,10 +529,11 @@ def run_bench(args):
                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                        "traffic": traffic_for_headline()}
     if not args.no_extras:
-        log("measured ceilings (1 GiB copy and read probes)")
-        cp, rd = probe_ceilings()
-        rec["probe_ceilings_gbs"] = {"copy": round(cp, 1), "read_only": round(rd, 1)}
-        log("decode latency, T = 1..64 (H=6144, K=8), graph of 100 calls")
+        log("measured ceilings (1 GiB copy, read and write probes)")
+        cp, rd, wr = probe_ceilings()
+        rec["probe_ceilings_gbs"] = {"copy": round(cp, 1), "read_only": round(rd, 1),
+                                     "write_only": round(wr, 1)}
+        log("decode latency, T = 1..64 (H=6144, K=8), graph-replayed, same and fresh inputs")
         rec["decode_latency_us"] = decode_latency()
         log("512-token batch, cold and warm")
         rec["batch_512"] = graph_ceiling_batch()

@@ -1,7 +1,8 @@
 // Bandwidth probes of known byte counts, used only by the benchmark: a plain
 // device copy (to calibrate the FETCH_SIZE / WRITE_SIZE counters against a
-// kernel whose traffic is known, and as a measured read+write ceiling) and a
-// read-only sweep (a read ceiling). Not part of the fused op.
+// kernel whose traffic is known, and as a measured read+write ceiling), a
+// read-only sweep (a read ceiling), a write-only fill (a write ceiling), and
+// an empty kernel (the per-launch floor). Not part of the fused op.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,7 +32,10 @@ __global__ __launch_bounds__(kThreads) void mfr_copy_probe_kernel(const u32x4* _
 }
 
 // Reads n vectors and writes one dword per workgroup (so the reads cannot be
-// removed); out must hold gridDim.x dwords.
+// removed); out must hold gridDim.x dwords. NT: non-temporal loads (the read
+// ceiling) or ordinary loads (which leave the data resident in the caches,
+// to set a known cache state).
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void mfr_read_probe_kernel(const u32x4* __restrict__ src,
                                                                   uint32_t* __restrict__ out,
                                                                   int64_t n) {
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void mfr_read_probe_kernel(const u32x4* _
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t i = base + u * kThreads + threadIdx.x;
-            v[u] = i < n ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+            v[u] = i < n ? (NT ? __builtin_nontemporal_load(src + i) : src[i]) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -57,6 +61,24 @@ __global__ __launch_bounds__(kThreads) void mfr_read_probe_kernel(const u32x4* _
         out[blockIdx.x] = r;
     }
 }
+
+// Writes n vectors of one constant pattern.
+__global__ __launch_bounds__(kThreads) void mfr_write_probe_kernel(u32x4* __restrict__ dst,
+                                                                   int64_t n, uint32_t pattern) {
+    const int64_t chunk = static_cast<int64_t>(kThreads) * kUnroll;
+    const u32x4 v = {pattern, pattern, pattern, pattern};
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * chunk; base < n;
+         base += static_cast<int64_t>(gridDim.x) * chunk) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + u * kThreads + threadIdx.x;
+            if (i < n) dst[i] = v;
+        }
+    }
+}
+
+// Does nothing: its launch-to-completion time is the floor under any kernel.
+__global__ void mfr_empty_probe_kernel() {}
 
 // Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) on
 // `stream` with `grid` workgroups of 256 threads. Returns 0 on success, 1 on
@@ -77,7 +99,38 @@ extern "C" int mfr_read_probe(const void* src, void* out, int64_t bytes, int gri
     if (!src || !out || bytes < 0 || (bytes & 15) || grid <= 0) return 1;
     if (reinterpret_cast<uintptr_t>(src) & 15) return 1;
     if (bytes == 0) return 0;
-    hipLaunchKernelGGL(mfr_read_probe_kernel, dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(mfr_read_probe_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const u32x4*>(src), static_cast<uint32_t*>(out), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// As mfr_read_probe, with ordinary (cache-allocating) loads.
+extern "C" int mfr_touch_probe(const void* src, void* out, int64_t bytes, int grid,
+                               hipStream_t stream) {
+    if (!src || !out || bytes < 0 || (bytes & 15) || grid <= 0) return 1;
+    if (reinterpret_cast<uintptr_t>(src) & 15) return 1;
+    if (bytes == 0) return 0;
+    hipLaunchKernelGGL(mfr_read_probe_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4*>(src), static_cast<uint32_t*>(out), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Fills `bytes` (a multiple of 16, 16-byte aligned) of dst with `pattern`
+// using `grid` workgroups of 256 threads. Returns 0 on success, 1 on bad
+// arguments, 2 if the launch failed.
+extern "C" int mfr_write_probe(void* dst, int64_t bytes, uint32_t pattern, int grid,
+                               hipStream_t stream) {
+    if (!dst || bytes < 0 || (bytes & 15) || grid <= 0) return 1;
+    if (reinterpret_cast<uintptr_t>(dst) & 15) return 1;
+    if (bytes == 0) return 0;
+    hipLaunchKernelGGL(mfr_write_probe_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<u32x4*>(dst), bytes / 16, pattern);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Launches the empty kernel with one workgroup of 64 threads. Returns 0 on
+// success, 2 if the launch failed.
+extern "C" int mfr_empty_probe(hipStream_t stream) {
+    hipLaunchKernelGGL(mfr_empty_probe_kernel, dim3(1), dim3(64), 0, stream);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
