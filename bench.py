@@ -584,6 +584,11 @@ def summarize_trace(args):
         short = name.replace("(mfr::Params)", "")
         lines.append(f"| `{short}` | {grid} | {wg} | {grid // wg} | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    if args.stats_csv:
+        with open(args.stats_csv) as f:
+            stats = f.read().strip()
+        lines += ["", "rocprofv3's own `--stats` summary of the same run (`*_kernel_stats.csv`, verbatim):",
+                  "", "```", stats, "```"]
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -643,6 +648,7 @@ def main():
     ap.add_argument("--summarize-pmc", action="store_true")
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
+    ap.add_argument("--stats-csv", default="", help="with --summarize-trace: append this kernel_stats.csv")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
