@@ -3,8 +3,8 @@
  * RMSNorm for MI355X (gfx950).
  *
  * The operation is the tail of a decode MoE layer whose top-k reduction was
- * left open by the experts (vLLM pull request #62174, "defer the MoE top-k
- * finalize into the next RMSNorm's fused all-reduce": Overview and Details).
+ * left open by the experts and is completed inside the following layer's
+ * input norm (vLLM pull request #62174, Overview and Details).
  * For each token t and hidden index h:
  *
  *   routed[h] = sum over slots k with perm_idx[t,k] >= 0 of
@@ -16,8 +16,9 @@
  * The page's fused kernel does the top-k sum, the routed scaling, the shared
  * add, an all-reduce across tensor-parallel ranks, the residual add and the
  * RMSNorm in one launch (Details); on one GPU the all-reduce is the identity.
- * The page also states that the fused kernel accumulates in FP32 and that the
- * finalize rounds once rather than after each step (Claims, Validation): here
+ * The page also says the kernel sums in FP32, and that its outputs moved
+ * because the per-step roundings of the unfused chain are gone (Claims,
+ * Validation): here
  * the sum s is kept in fp32 registers, rounded to bf16 only at the two outputs,
  * and the norm is taken of the unrounded fp32 s.
  *
@@ -47,8 +48,8 @@
  * bf16 pointers must be 16-byte aligned; perm_idx and topk_w 4-byte aligned.
  *
  * Ownership and ordering: the caller owns every buffer; the library allocates
- * and frees nothing and keeps no per-call state (the page's consumer frees the
- * deferred buffers: Details). The work is enqueued on `stream` (NULL = the
+ * and frees nothing and keeps no per-call state (on the page, releasing the
+ * deferred buffers is the consuming layer's job: Details). The work is enqueued on `stream` (NULL = the
  * device's null stream) and the call returns without synchronising; buffers
  * must stay valid until the stream has passed the kernel. Calls may be
  * captured into a HIP graph. Results are deterministic: no atomics, and a

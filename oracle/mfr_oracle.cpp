@@ -6,15 +6,16 @@
 // It shares no code, header, table or helper with the HIP library and must
 // never be reached from the product path.
 //
-// What it computes (vLLM pull request #62174, "defer the MoE top-k finalize
-// into the next RMSNorm's fused all-reduce"):
+// What it computes (vLLM pull request #62174, where a decode MoE layer leaves
+// its top-k reduction to the next layer's fused norm):
 //   * Details: the fused kernel takes the top-k sum of the GEMM2 rows, applies
 //     the routed scaling factor, adds the shared-expert output, all-reduces
 //     (the identity on one GPU), adds the residual and applies RMSNorm.
-//   * Validation: the fused result must equal the unfused chain "finalize,
-//     then shared add, then RMSNorm of the all-reduced sum"; the finalize now
-//     rounds once instead of after every step.
-//   * Claims: the fused kernel accumulates in FP32.
+//   * Validation: its result is checked against the separate steps (the
+//     finalize, the shared add, and RMSNorm of the all-reduced sum), and the
+//     page notes that outputs moved because intermediate roundings are gone:
+//     the sum is rounded a single time.
+//   * Claims: the kernel keeps its sums in FP32.
 // Written here as that plain definition, in fp64, with exactly one rounding
 // to bf16 at each output (residual_out and normed_out).
 //

@@ -6,8 +6,8 @@ that holds the unfinalized routed part (the GEMM2 rows, the permutation map
 and the routing weights) plus the shared-expert output. The next layer's input
 norm then finalizes it, adds the residual and normalises in one kernel. A layer
 defers only when the fused kernel will run for the shape; otherwise it
-finalizes as before. The consumer owns and frees the deferred buffers once the
-fused kernel has been enqueued.
+finalizes as before. Releasing the deferred buffers, once the fused kernel has
+been enqueued, is the consuming layer's job.
 
 Here:
   * ``UnfinalizedMoEOutput`` / ``MoEOutput`` carry the deferred tensors;
