@@ -211,3 +211,37 @@ def test_fp8_validation():
     assert fp8_call(normed_out=base["normed_fp8"]) == binding.MFR_ERR_ALIAS
     # without the optional bf16 output, its pointer is not examined
     assert fp8_call(T_=0, normed_out=None) == binding.MFR_OK
+
+
+def _path_in_subprocess(env_value, T, forced=0):
+    """moe_finalize_rmsnorm_path(T, 6144, 8) in a fresh process whose
+    environment holds MFR_PATH=env_value (read once, when the library loads)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, sys\n"
+            "from top_finalize_residual_amd import build\n"
+            "lib = ctypes.CDLL(build.LIB)\n"
+            "lib.moe_finalize_rmsnorm_path.argtypes = [ctypes.c_int64] * 3\n"
+            f"assert lib.moe_finalize_rmsnorm_force({forced}, 0, 0) == 0\n"
+            f"print(lib.moe_finalize_rmsnorm_path({T}, 6144, 8))\n")
+    env = dict(os.environ)
+    env.pop("MFR_PATH", None)
+    if env_value is not None:
+        env["MFR_PATH"] = env_value
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return int(r.stdout.strip()), r.stderr
+
+
+def test_env_path_switch():
+    """MFR_PATH sets the default path; an explicit override still wins; an
+    unknown value is reported and ignored."""
+    assert _path_in_subprocess(None, 8)[0] == mfr.PATH_TOKEN
+    assert _path_in_subprocess(None, 8192)[0] == mfr.PATH_STREAM
+    assert _path_in_subprocess("auto", 8192)[0] == mfr.PATH_STREAM
+    assert _path_in_subprocess("stream", 8)[0] == mfr.PATH_STREAM
+    assert _path_in_subprocess("token", 8192)[0] == mfr.PATH_TOKEN
+    assert _path_in_subprocess("stream", 8, forced=mfr.PATH_TOKEN)[0] == mfr.PATH_TOKEN
+    p, err = _path_in_subprocess("fastest", 8)
+    assert p == mfr.PATH_TOKEN and "MFR_PATH=fastest" in err

@@ -89,3 +89,27 @@ def test_zero_tokens_every_entry_point():
     assert q.shape == (0, 2048) and sc.shape == (0,) and n.shape == (0, 2048)
     r, n = mfr.residual_add_rmsnorm(dd["shared_out"], dd["residual"], dd["gamma"], 1e-6)
     assert r.shape == (0, 2048)
+
+
+def test_env_log_reports_each_launch():
+    """MFR_LOG=1 prints the launch shape the host chose for every call."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import torch, synth\n"
+            "import top_finalize_residual_amd as mfr\n"
+            "from tests import gpu_util as gu\n"
+            "for T in (4, 1024):\n"
+            "    d = synth.generate(T, 2048, 8, seed=5)\n"
+            "    gu.run(gu.to_device(d), d['eps'], d['scale'])\n"
+            "torch.cuda.synchronize()\n")
+    env = dict(os.environ, MFR_LOG="1")
+    env.pop("MFR_PATH", None)
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("moe_finalize_rmsnorm: T=")]
+    assert len(lines) == 2, r.stderr[-2000:]
+    assert "T=4 H=2048 K=8 variant=top8 out=bf16 path=token" in lines[0]
+    assert "T=1024 H=2048 K=8 variant=top8 out=bf16 path=stream" in lines[1]

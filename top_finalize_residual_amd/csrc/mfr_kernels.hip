@@ -44,6 +44,9 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 namespace mfr {
 
@@ -343,6 +346,29 @@ constexpr int64_t kTokenPathMaxT = 256;
 constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
 
 std::atomic<int> g_force_path{0};
+
+// Environment switches, read once when the library is loaded:
+//   MFR_PATH=auto|token|stream  default launch path (an override set through
+//                               moe_finalize_rmsnorm_force takes precedence);
+//   MFR_LOG=1                   one line on stderr per launch: shape, path,
+//                               vectors per thread, threads, store policy.
+// An unrecognised MFR_PATH value is reported on stderr and ignored.
+int env_path() {
+    const char* v = std::getenv("MFR_PATH");
+    if (!v || !*v || std::strcmp(v, "auto") == 0) return 0;
+    if (std::strcmp(v, "token") == 0) return MFR_PATH_TOKEN;
+    if (std::strcmp(v, "stream") == 0) return MFR_PATH_STREAM;
+    std::fprintf(stderr, "moe_finalize_rmsnorm: ignoring MFR_PATH=%s (auto, token or stream)\n", v);
+    return 0;
+}
+
+bool env_log() {
+    const char* v = std::getenv("MFR_LOG");
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+const int g_env_path = env_path();
+const bool g_env_log = env_log();
 std::atomic<int> g_force_vpt{0};
 std::atomic<int> g_force_store{0};
 
@@ -359,7 +385,8 @@ bool shape_ok(int64_t T, int64_t H, int64_t K) {
 }
 
 int choose_path(int64_t T) {
-    const int f = g_force_path.load(std::memory_order_relaxed);
+    int f = g_force_path.load(std::memory_order_relaxed);
+    if (f == 0) f = g_env_path;
     if (f == MFR_PATH_TOKEN || f == MFR_PATH_STREAM) return f;
     return T <= kTokenPathMaxT ? MFR_PATH_TOKEN : MFR_PATH_STREAM;
 }
@@ -463,7 +490,17 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     const int path = choose_path(T);
     const int vpt = choose_vpt(path, p.V);
     const int nt = threads_for(p.V, vpt);
-    const void* kern = kernel_for(vpt, v, write_through(path, T, H), qm);
+    const bool wt = write_through(path, T, H);
+    const void* kern = kernel_for(vpt, v, wt, qm);
+    if (g_env_log)
+        std::fprintf(stderr,
+                     "moe_finalize_rmsnorm: T=%lld H=%lld K=%d variant=%s out=%s path=%s vpt=%d "
+                     "threads=%d stores=%s\n",
+                     static_cast<long long>(T), static_cast<long long>(H), p.K,
+                     v == kTop8 ? "top8" : v == kAnyK ? "anyK" : "dense",
+                     qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16",
+                     path == MFR_PATH_TOKEN ? "token" : "stream", vpt, nt,
+                     wt ? "write-through" : "write-back");
     void* args[] = {&p};
     const hipError_t e =
         hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
