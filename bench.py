@@ -23,10 +23,10 @@ Modes used with rocprofv3 (see profiles/):
 """
 import argparse
 import csv
-import glob
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -44,16 +44,34 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """Hash of the fused kernel's sources (not the probes): traffic figures
-    measured on an older version of the kernel are not reported."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "top_finalize_residual_amd", "csrc")
-    for p in sorted(glob.glob(os.path.join(csrc, "mfr_*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def _elf_section(path, name):
+    """Bytes of one section of a 64-bit little-endian ELF file, or None."""
+    with open(path, "rb") as f:
+        b = f.read()
+    if b[:4] != b"\x7fELF" or b[4] != 2 or b[5] != 1:
+        return None
+    shoff, = struct.unpack_from("<Q", b, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+
+    def header(i):
+        return struct.unpack_from("<IIQQQQIIQQ", b, shoff + i * shentsize)
+    strtab = header(shstrndx)
+    names = b[strtab[4]:strtab[4] + strtab[5]]
+    for i in range(shnum):
+        h = header(i)
+        if names[h[0]:names.index(b"\0", h[0])].decode() == name:
+            return b[h[4]:h[4] + h[5]]
+    return None
+
+
+def kernel_code_hash():
+    """Hash of the gfx950 code objects embedded in the built library (the
+    .hip_fatbin section): it changes exactly when the kernels' machine code
+    does, and not for host-only edits. Traffic figures measured on other
+    kernel code are not reported."""
+    from top_finalize_residual_amd import build as b
+    sec = _elf_section(b.LIB, ".hip_fatbin") if os.path.exists(b.LIB) else None
+    return hashlib.sha256(sec).hexdigest()[:16] if sec else None
 
 
 # ---------------------------------------------------------------------------
@@ -239,7 +257,8 @@ def traffic_for_headline():
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    code = kernel_code_hash()
+    if code is None or t.get("code_hash") != code:
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -623,7 +642,7 @@ def summarize_pmc(args):
     d = synth.config_inputs(HEADLINE_CFG, HEADLINE_T)
     alg = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     traffic = f_fused * 1024.0 * cf + w_fused * 1024.0 * cw
-    out = {"kernel": fk, "source_hash": kernel_source_hash(),
+    out = {"kernel": fk, "code_hash": kernel_code_hash(),
            "fetch_kib_per_dispatch": f_fused, "write_kib_per_dispatch": w_fused,
            "copy_probe": {"bytes": copy_bytes, "fetch_kib": f_copy, "write_kib": w_copy,
                           "fetch_scale": cf, "write_scale": cw},
