@@ -32,6 +32,8 @@ def test_custom_ops_are_registered_with_fake_kernels():
     from torch._subclasses.fake_tensor import FakeTensorMode
     assert hasattr(torch.ops.mfr, "moe_finalize_rmsnorm")
     assert hasattr(torch.ops.mfr, "residual_add_rmsnorm")
+    assert hasattr(torch.ops.mfr, "moe_finalize_rmsnorm_")
+    assert hasattr(torch.ops.mfr, "residual_add_rmsnorm_")
     with FakeTensorMode():
         x = torch.empty(4, 64, dtype=torch.bfloat16)
         r, n = mfr.fused_add_rmsnorm(x, torch.empty_like(x), torch.empty(64, dtype=torch.bfloat16),

@@ -68,6 +68,36 @@ def test_custom_ops_pass_opcheck():
     torch.library.opcheck(torch.ops.mfr.residual_add_rmsnorm.default,
                           (dd["shared_out"], dd["residual"], dd["gamma"], d["eps"], ro, no),
                           test_utils=("test_schema", "test_faketensor"))
+    # the in-place forms: the residual stream is the one mutated argument
+    torch.library.opcheck(torch.ops.mfr.moe_finalize_rmsnorm_.default,
+                          (dd["expert_out"], dd["perm_idx"], dd["topk_w"], dd["shared_out"],
+                           dd["residual"].clone(), dd["gamma"], d["eps"], d["scale"], no),
+                          test_utils=("test_schema", "test_faketensor"))
+    torch.library.opcheck(torch.ops.mfr.residual_add_rmsnorm_.default,
+                          (dd["shared_out"], dd["residual"].clone(), dd["gamma"], d["eps"], no),
+                          test_utils=("test_schema", "test_faketensor"))
+
+
+@pytest.mark.parametrize("deferred", [True, False], ids=["moe", "dense"])
+def test_in_place_forms_equal_out_of_place(deferred):
+    """in_place=True and residual_out=residual both update the residual
+    stream through the in-place op, bit-identical to the out-of-place op."""
+    d = synth.generate(28, 6144, 8, scale=2.5, seed=67)
+    dd, u = _dev(d)
+    hidden = mfr.MoEOutput(u, dd["shared_out"]) if deferred else dd["shared_out"]
+    r0, n0 = mfr.fused_add_rmsnorm(hidden, dd["residual"], dd["gamma"], d["eps"])
+    for kw in ({"in_place": True}, {"residual_out": "self"}):
+        res = dd["residual"].clone()
+        if kw.get("residual_out") == "self":
+            kw = {"residual_out": res}
+        r, n = mfr.fused_add_rmsnorm(hidden, res, dd["gamma"], d["eps"], **kw)
+        torch.cuda.synchronize()
+        assert r is res
+        assert torch.equal(r.view(torch.int16), r0.view(torch.int16))
+        assert torch.equal(n.view(torch.int16), n0.view(torch.int16))
+    with pytest.raises(ValueError, match="in_place"):
+        mfr.fused_add_rmsnorm(hidden, dd["residual"], dd["gamma"], d["eps"], in_place=True,
+                              residual_out=torch.empty_like(dd["residual"]))
 
 
 def test_decoder_tail_graph_replay():

@@ -72,6 +72,14 @@ def test_binding_rejects_bad_tensors_before_launch():
     with pytest.raises(ValueError):
         mfr.moe_finalize_rmsnorm(*args, d["eps"], d["scale"],
                                  residual_out=torch.empty(4, 2048, dtype=torch.bfloat16))
+    # FP8 outputs of the wrong length are refused before anything is written
+    with pytest.raises(ValueError, match="fp8_scale"):
+        mfr.moe_finalize_rmsnorm_fp8(*args, d["eps"], d["scale"],
+                                     fp8_scale=torch.empty(3, device="cuda"))
+    with pytest.raises(ValueError, match="normed_out"):
+        mfr.moe_finalize_rmsnorm_fp8(*args, d["eps"], d["scale"],
+                                     normed_out=torch.empty(3, 2048, dtype=torch.bfloat16,
+                                                            device="cuda"))
     # a masked-everything call with NaN weights still works (weights of masked slots ignored)
     p = torch.full_like(dd["perm_idx"], -1)
     w = torch.full_like(dd["topk_w"], float("nan"))

@@ -4,6 +4,7 @@ Every step of the op runs in the HIP library. torch supplies device memory and
 the current stream. There is no CPU fallback: if the library is missing,
 importing this module raises.
 """
+import contextlib
 import ctypes
 import os
 
@@ -105,6 +106,19 @@ def _same_device(*tensors):
         raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
 
 
+def _launch_context(dev, stream):
+    """The stream to launch on (the device's current stream by default) and a
+    context that makes the tensors' GPU current for the call: the library
+    launches on the calling thread's current device."""
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return stream, contextlib.nullcontext()
+    return stream, torch.cuda.device(dev)
+
+
 def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
                          residual_out=None, normed_out=None, stream=None):
     """Fused MoE finalize + residual add + RMSNorm on the current (or given) stream.
@@ -138,12 +152,12 @@ def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gam
     if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
         raise ValueError("outputs must be [T, H]")
     _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out, normed_out)
-    if stream is None:
-        stream = torch.cuda.current_stream(residual.device)
-    rc = _lib.moe_finalize_rmsnorm(
-        expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
-        residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale),
-        residual_out.data_ptr(), normed_out.data_ptr(), T, H, K, stream.cuda_stream)
+    stream, ctx = _launch_context(residual.device, stream)
+    with ctx:
+        rc = _lib.moe_finalize_rmsnorm(
+            expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
+            residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale),
+            residual_out.data_ptr(), normed_out.data_ptr(), T, H, K, stream.cuda_stream)
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_out
@@ -176,11 +190,11 @@ def residual_add_rmsnorm(x, residual, gamma, eps, residual_out=None, normed_out=
     if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
         raise ValueError("outputs must be [T, H]")
     _same_device(x, residual, gamma, residual_out, normed_out)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
-    rc = _lib.residual_add_rmsnorm(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
-                                   residual_out.data_ptr(), normed_out.data_ptr(), T, H,
-                                   stream.cuda_stream)
+    stream, ctx = _launch_context(x.device, stream)
+    with ctx:
+        rc = _lib.residual_add_rmsnorm(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
+                                       float(eps), residual_out.data_ptr(), normed_out.data_ptr(),
+                                       T, H, stream.cuda_stream)
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_out
@@ -228,18 +242,24 @@ def moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual,
     if normed_fp8.dtype not in (torch.float8_e4m3fn, torch.uint8) or not normed_fp8.is_cuda or \
             not normed_fp8.is_contiguous() or tuple(normed_fp8.shape) != (T, H):
         raise ValueError("normed_fp8 must be a contiguous [T, H] float8_e4m3fn (or uint8) GPU tensor")
+    if tuple(residual_out.shape) != (T, H):
+        raise ValueError("residual_out must be [T, H]")
     _check(fp8_scale, "fp8_scale", torch.float32, 1)
+    if tuple(fp8_scale.shape) != (T,):
+        raise ValueError(f"fp8_scale has shape {tuple(fp8_scale.shape)}, expected {(T,)}")
     if normed_out is not None:
         _check(normed_out, "normed_out", torch.bfloat16, 2)
+        if tuple(normed_out.shape) != (T, H):
+            raise ValueError("normed_out must be [T, H]")
     _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out,
                  normed_fp8, fp8_scale, normed_out)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    rc = _lib.moe_finalize_rmsnorm_fp8(
-        expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
-        residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale), residual_out.data_ptr(),
-        normed_out.data_ptr() if normed_out is not None else None, normed_fp8.data_ptr(),
-        fp8_scale.data_ptr(), T, H, K, stream.cuda_stream)
+    stream, ctx = _launch_context(dev, stream)
+    with ctx:
+        rc = _lib.moe_finalize_rmsnorm_fp8(
+            expert_out.data_ptr(), perm_idx.data_ptr(), topk_w.data_ptr(), shared_out.data_ptr(),
+            residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale),
+            residual_out.data_ptr(), normed_out.data_ptr() if normed_out is not None else None,
+            normed_fp8.data_ptr(), fp8_scale.data_ptr(), T, H, K, stream.cuda_stream)
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_fp8, fp8_scale, normed_out

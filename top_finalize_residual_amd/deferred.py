@@ -16,9 +16,12 @@ Here:
   * ``fused_add_rmsnorm(hidden, residual, gamma, eps)`` is the consumer norm:
     a deferred MoEOutput goes to the fused finalize kernel, a plain tensor
     (attention / dense MLP output) to the dense residual add + RMSNorm kernel;
-  * both kernels are registered as torch custom ops (``mfr::moe_finalize_rmsnorm``
-    and ``mfr::residual_add_rmsnorm``) that write into caller-provided outputs, so
-    torch sees their effects and CUDA/HIP graph capture records them.
+  * both kernels are registered as torch custom ops that write into
+    caller-provided outputs, so torch sees their effects and HIP graph capture
+    records them: ``mfr::moe_finalize_rmsnorm`` and ``mfr::residual_add_rmsnorm``
+    write a separate residual_out; ``mfr::moe_finalize_rmsnorm_`` and
+    ``mfr::residual_add_rmsnorm_`` update the residual stream in place (it is
+    then the one mutated argument, never passed twice).
 Every step of the arithmetic runs in the HIP library; nothing here computes.
 """
 from dataclasses import dataclass
@@ -50,6 +53,25 @@ def _residual_add_rmsnorm_op(x: torch.Tensor, residual: torch.Tensor, gamma: tor
                                  normed_out=normed_out)
 
 
+@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm_",
+                         mutates_args=("residual", "normed_out"))
+def _moe_finalize_rmsnorm_inplace_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
+                                     topk_w: torch.Tensor, shared_out: torch.Tensor,
+                                     residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                                     scale: float, normed_out: torch.Tensor) -> None:
+    binding.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
+                                 scale, residual_out=residual, normed_out=normed_out)
+
+
+@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm_",
+                         mutates_args=("residual", "normed_out"))
+def _residual_add_rmsnorm_inplace_op(x: torch.Tensor, residual: torch.Tensor,
+                                     gamma: torch.Tensor, eps: float,
+                                     normed_out: torch.Tensor) -> None:
+    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual,
+                                 normed_out=normed_out)
+
+
 @_moe_finalize_rmsnorm_op.register_fake
 def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
       normed_out):
@@ -58,6 +80,16 @@ def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, res
 
 @_residual_add_rmsnorm_op.register_fake
 def _(x, residual, gamma, eps, residual_out, normed_out):
+    return None
+
+
+@_moe_finalize_rmsnorm_inplace_op.register_fake
+def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, normed_out):
+    return None
+
+
+@_residual_add_rmsnorm_inplace_op.register_fake
+def _(x, residual, gamma, eps, normed_out):
     return None
 
 
@@ -106,11 +138,16 @@ def defer_moe_finalize(num_tokens: int, hidden_size: int, top_k: int) -> bool:
 
 
 def _outputs(ref: torch.Tensor, residual: torch.Tensor, residual_out, normed_out, in_place):
-    if residual_out is None:
-        residual_out = residual if in_place else torch.empty_like(ref)
+    """(residual_out or None for an in-place update, normed_out)."""
+    if residual_out is residual:
+        in_place = True
+    elif in_place and residual_out is not None:
+        raise ValueError("in_place=True writes the residual stream itself; pass no residual_out")
+    if not in_place and residual_out is None:
+        residual_out = torch.empty_like(ref)
     if normed_out is None:
         normed_out = torch.empty_like(ref)
-    return residual_out, normed_out
+    return (None if in_place else residual_out), normed_out
 
 
 def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Tensor,
@@ -123,28 +160,35 @@ def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Te
     hidden: a MoEOutput (deferred or finalized routed part plus shared output)
     or a plain [T, H] bf16 tensor (a dense layer's output).
     Returns (new residual stream, normed hidden state), both [T, H] bf16.
-    in_place: write the new residual stream into `residual` itself.
+    in_place: write the new residual stream into `residual` itself (also
+    implied by passing residual_out=residual).
     """
     if isinstance(hidden, MoEOutput):
         shared = hidden.shared
         residual_out, normed_out = _outputs(shared, residual, residual_out, normed_out, in_place)
         if hidden.deferred:
             r = hidden.routed
-            torch.ops.mfr.moe_finalize_rmsnorm(r.expert_out, r.perm_idx, r.topk_w, shared,
-                                               residual, gamma, float(eps), float(r.scale),
-                                               residual_out, normed_out)
+            rows, idx, w, scale = r.expert_out, r.perm_idx, r.topk_w, float(r.scale)
         else:
             # An already finalized routed part goes through the same kernel as
             # a single routed row per token (weight 1, scale 1), which keeps
             # the one-rounding contract for routed + shared + residual.
-            routed = hidden.routed
-            T = routed.shape[0]
-            ident = torch.arange(T, dtype=torch.int32, device=routed.device).unsqueeze(1)
-            ones = torch.ones((T, 1), dtype=torch.float32, device=routed.device)
-            torch.ops.mfr.moe_finalize_rmsnorm(routed, ident, ones, shared, residual, gamma,
-                                               float(eps), 1.0, residual_out, normed_out)
+            rows = hidden.routed
+            T = rows.shape[0]
+            idx = torch.arange(T, dtype=torch.int32, device=rows.device).unsqueeze(1)
+            w = torch.ones((T, 1), dtype=torch.float32, device=rows.device)
+            scale = 1.0
+        if residual_out is None:
+            torch.ops.mfr.moe_finalize_rmsnorm_(rows, idx, w, shared, residual, gamma, float(eps),
+                                                scale, normed_out)
+            return residual, normed_out
+        torch.ops.mfr.moe_finalize_rmsnorm(rows, idx, w, shared, residual, gamma, float(eps), scale,
+                                           residual_out, normed_out)
         return residual_out, normed_out
     residual_out, normed_out = _outputs(hidden, residual, residual_out, normed_out, in_place)
+    if residual_out is None:
+        torch.ops.mfr.residual_add_rmsnorm_(hidden, residual, gamma, float(eps), normed_out)
+        return residual, normed_out
     torch.ops.mfr.residual_add_rmsnorm(hidden, residual, gamma, float(eps), residual_out,
                                        normed_out)
     return residual_out, normed_out
