@@ -238,6 +238,47 @@ def test_graph_capture_replay():
         assert np.array_equal(gu.host_u16(n_out), n_eager), i
 
 
+def test_graph_back_to_back_in_place_chain():
+    """1000 graph replays launched back to back with no synchronisation,
+    each updating the residual stream in place, so that every replay reads
+    what the previous one wrote. The final state must equal, bit for bit,
+    1000 eager calls: nothing carries over between launches except the
+    data, and no launch may start before the previous one finished."""
+    d = synth.config_inputs("decode", 4)
+    dd = gu.to_device(d)
+    n_out = torch.empty_like(dd["residual"])
+
+    def step(res):
+        mfr.moe_finalize_rmsnorm(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
+                                 dd["shared_out"], res, dd["gamma"], d["eps"], d["scale"],
+                                 residual_out=res, normed_out=n_out)
+    eager = dd["residual"].clone()
+    for _ in range(1000):
+        step(eager)
+    torch.cuda.synchronize()
+    want_res, want_n = gu.host_u16(eager), gu.host_u16(n_out)
+
+    chained = dd["residual"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(chained.clone())  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(chained)
+    torch.cuda.synchronize()
+    chained.copy_(dd["residual"])
+    n_out.fill_(0)
+    torch.cuda.synchronize()
+    for _ in range(1000):
+        g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_u16(chained), want_res)
+    assert np.array_equal(gu.host_u16(n_out), want_n)
+    assert not np.array_equal(want_res, gu.host_u16(dd["residual"]))
+
+
 def test_row_offsets_beyond_2gib():
     """expert_out larger than 2^31 bytes: rows past that mark are gathered with
     64-bit row offsets. Only the referenced rows are filled; the others are
