@@ -471,6 +471,20 @@ def pin_e4m3_vs_torch(o):
     assert np.array_equal(o.rne_e4m3_from_f64(x.astype(np.float64)), ref)
 
 
+def pin_e4m3_nan(o):
+    """NaN has one E4M3 encoding, all exponent and mantissa bits set
+    (S.1111.111), with the sign kept. This is a library special case:
+    torch's float8_e4m3fn converter gives the same codes. In a row, a NaN
+    element keeps that code and takes no part in amax."""
+    x = np.array([np.nan, -np.nan], dtype=np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert ref.tolist() == [0x7F, 0xFF]
+    assert np.array_equal(o.rne_e4m3_from_f64(x.astype(np.float64)), ref)
+    codes, scales, _ = o.fp8_quantize_rows(np.array([[1.0, np.nan, -7.0, 0.5]]))
+    assert scales.tolist() == [7.0 / 448.0]
+    assert (codes[0, 1] & 0x7F) == 0x7F and codes[0, 2] == 0xFE
+
+
 def pin_e4m3_vs_exact(o):
     """Doubles that are not binary32 values, against exact rational search."""
     rng = np.random.default_rng(19)
@@ -521,5 +535,6 @@ ALL_PINS = [
     pin_scale_invariance, pin_unit_rms, pin_masked_nan_poison, pin_weight_zero_reads_row,
     pin_index_range, pin_dense_hand_case, pin_dense_bruteforce_exact, pin_dense_rms_norm_library,
     pin_dense_equals_all_masked_finalize, pin_e4m3_roundtrip, pin_e4m3_midpoints_and_saturation,
-    pin_e4m3_vs_torch, pin_e4m3_vs_exact, pin_fp8_hand_case, pin_fp8_quantize_properties,
+    pin_e4m3_vs_torch, pin_e4m3_nan, pin_e4m3_vs_exact, pin_fp8_hand_case,
+    pin_fp8_quantize_properties,
 ]

@@ -52,6 +52,22 @@ MUTANTS = [
     ("e4m3_subnormal_spacing", "if (lead < -6) lead = -6;", "if (lead < -7) lead = -7;"),
     ("fp8_scale_from_first_element", "amax = std::fmax(amax, std::fabs(y[t * H + h]));",
      "amax = std::fabs(y[t * H]);"),
+    ("masked_slot_reads_row0", "if (idx < 0) continue;", "const int64_t r0 = idx < 0 ? 0 : idx;\n"
+     "            if (r0 >= R) return MFR_ORACLE_ERR_INDEX;\n"
+     "            const double w0 = static_cast<double>(topk_w[t * K + k]);\n"
+     "            for (int64_t h = 0; h < H; ++h) routed[h] += w0 * bf16_bits_to_double(expert_out[r0 * H + h]);\n"
+     "            continue;"),
+    ("last_slot_dropped", "for (int64_t k = 0; k < K; ++k) {\n            const int64_t idx",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n            const int64_t idx"),
+    ("bf16_nan_to_zero", "if (std::isnan(x)) return static_cast<uint16_t>(sign | 0x7FC0u);",
+     "if (std::isnan(x)) return sign;"),
+    ("bf16_overflow_to_max_finite", "if (y >= 0x1p128) return static_cast<uint16_t>(sign | 0x7F80u);",
+     "if (y >= 0x1p128) return static_cast<uint16_t>(sign | 0x7F7Fu);"),
+    ("e4m3_nan_to_zero", "if (std::isnan(v)) return static_cast<uint8_t>(sign | 0x7Fu);",
+     "if (std::isnan(v)) return sign;"),
+    ("fp8_zero_row_scale_zero", "amax > 0.0 ? amax / 448.0 : 1.0", "amax > 0.0 ? amax / 448.0 : 0.0"),
+    ("fp8_amax_signed", "amax = std::fmax(amax, std::fabs(y[t * H + h]));",
+     "amax = std::fmax(amax, y[t * H + h]);"),
 ]
 
 
