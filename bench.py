@@ -282,7 +282,9 @@ def stacked_calls(d, n, mode="bf16"):
     dd = to_device(d)
     T, K = dd["perm_idx"].shape
     H = dd["gamma"].shape[0]
-    st = {k: v.unsqueeze(0).repeat((n,) + (1,) * v.dim()) for k, v in dd.items()}
+    # one set: the uploaded tensors themselves; more: copies made on the device
+    st = {k: (v.unsqueeze(0) if n == 1 else v.unsqueeze(0).repeat((n,) + (1,) * v.dim()))
+          for k, v in dd.items()}
     ro = torch.empty((n, T, H), dtype=torch.bfloat16, device="cuda")
     no = torch.empty_like(ro)
     q = torch.empty((n, T, H), dtype=torch.uint8, device="cuda")
@@ -484,24 +486,30 @@ def deferred_overhead():
 
 
 def run_latency(args):
-    """Eager calls at the decode sizes and the 512 batch, for a kernel trace."""
+    """Eager calls for a kernel trace, small sizes first so that no large call
+    has flushed the caches before them: the fused op at the decode sizes, the
+    FP8-output call and the dense tail at T = 28, the 512-token batch, then
+    the dense tail and the FP8-output call at T = 8192."""
     import torch
     import synth
     torch.cuda.set_device(0)
-    for cfg, T in [("decode", t) for t in DECODE_TS] + [("batch512", 512)]:
-        d = synth.config_inputs(cfg, T)
-        dd = to_device(d)
-        call, _ = make_caller(dd, d["eps"], d["scale"])
-        for _ in range(args.steps):
+
+    def run(call, n, what):
+        for _ in range(n):
             call()
         torch.cuda.synchronize()
-        log(f"T={T}: {args.steps} calls")
-    for T in (28, 8192):
-        call = make_dense_caller(synth.dense_inputs(T, 6144, seed=synth.seed_for("prefill", T)))
-        for _ in range(args.steps if T < 8192 else 20):
-            call()
-        torch.cuda.synchronize()
-        log(f"dense T={T}")
+        log(f"{what}: {n} calls")
+    for T in DECODE_TS:
+        d = synth.config_inputs("decode", T)
+        run(make_caller(to_device(d), d["eps"], d["scale"])[0], args.steps, f"T={T}")
+    run(stacked_calls(synth.config_inputs("decode", 28), 1, "fp8")[0], args.steps, "fp8 output T=28")
+    run(make_dense_caller(synth.dense_inputs(28, 6144, seed=synth.seed_for("prefill", 28))),
+        args.steps, "dense T=28")
+    d = synth.config_inputs("batch512", 512)
+    run(make_caller(to_device(d), d["eps"], d["scale"])[0], args.steps, "T=512")
+    run(make_dense_caller(synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192))),
+        20, "dense T=8192")
+    run(stacked_calls(synth.config_inputs("prefill", 8192), 1, "fp8")[0], 20, "fp8 output T=8192")
 
 
 def run_bench(args):
