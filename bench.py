@@ -175,35 +175,39 @@ def _probe_lib():
 def probe_ceilings(nbytes=1 << 30, reps=10):
     """GB/s of the copy probe (read + write bytes), the read-only probe and
     the write-only probe, on 1 GiB buffers (4x the Infinity Cache, so all
-    three stream from HBM)."""
+    three stream from HBM). Each is the best over three grid sizes (2, 8 and
+    32 workgroups per CU): the write rate in particular depends on it."""
     import torch
     lib = _probe_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    grid = cus * 8
-    sink = torch.empty(grid, dtype=torch.int32, device="cuda")
+    grids = (cus * 2, cus * 8, cus * 32)
+    sink = torch.empty(max(grids), dtype=torch.int32, device="cuda")
+    best = {"copy": 0.0, "read": 0.0, "write": 0.0}
+    for grid in grids:
+        def copy():
+            if lib.mfr_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, grid,
+                                  torch.cuda.current_stream().cuda_stream) != 0:
+                raise RuntimeError("copy probe failed")
 
-    def copy():
-        if lib.mfr_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, grid,
-                              torch.cuda.current_stream().cuda_stream) != 0:
-            raise RuntimeError("copy probe failed")
+        def read():
+            if lib.mfr_read_probe(src.data_ptr(), sink.data_ptr(), nbytes, grid,
+                                  torch.cuda.current_stream().cuda_stream) != 0:
+                raise RuntimeError("read probe failed")
 
-    def read():
-        if lib.mfr_read_probe(src.data_ptr(), sink.data_ptr(), nbytes, grid,
-                              torch.cuda.current_stream().cuda_stream) != 0:
-            raise RuntimeError("read probe failed")
-    def write():
-        if lib.mfr_write_probe(dst.data_ptr(), nbytes, 0x3F803F80, grid,
-                               torch.cuda.current_stream().cuda_stream) != 0:
-            raise RuntimeError("write probe failed")
-    copy_gbs = 2 * nbytes / (time_calls([copy], reps, 2) * 1e-3) / 1e9
-    read_gbs = nbytes / (time_calls([read], reps, 2) * 1e-3) / 1e9
-    write_gbs = nbytes / (time_calls([write], reps, 2) * 1e-3) / 1e9
+        def write():
+            if lib.mfr_write_probe(dst.data_ptr(), nbytes, 0x3F803F80, grid,
+                                   torch.cuda.current_stream().cuda_stream) != 0:
+                raise RuntimeError("write probe failed")
+        for name, fn, moved in (("copy", copy, 2 * nbytes), ("read", read, nbytes),
+                                ("write", write, nbytes)):
+            gbs = moved / (time_calls([fn], reps, 2) * 1e-3) / 1e9
+            best[name] = max(best[name], gbs)
     del src, dst, sink
     torch.cuda.empty_cache()
-    return copy_gbs, read_gbs, write_gbs
+    return best["copy"], best["read"], best["write"]
 
 
 def launch_floor_us():
