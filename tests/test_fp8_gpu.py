@@ -177,3 +177,43 @@ def test_fp8_nan_gamma_element():
     keep = np.arange(H) != col
     sub = dict(s=ref["s"][:, keep], normed_exact=ref["normed_exact"][:, keep])
     check_fp8(q[:, keep], sc, sub, d["gamma"][keep], d["eps"])
+
+
+def test_fp8_graph_replay():
+    """The FP8-output call captured into a graph replays like the eager call,
+    codes and scales bit for bit, with eager work and synchronisations
+    between the replays."""
+    d = synth.config_inputs("decode", 28)
+    dd = gu.to_device(d)
+    r0, q0, s0, n0 = run_fp8(dd, d, bf16_normed=True)
+    T, H = d["T"], d["H"]
+    ro = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    no = torch.empty_like(ro)
+    q = torch.empty((T, H), dtype=torch.float8_e4m3fn, device="cuda")
+    sc = torch.empty((T,), dtype=torch.float32, device="cuda")
+
+    def call():
+        mfr.moe_finalize_rmsnorm_fp8(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
+                                     dd["shared_out"], dd["residual"], dd["gamma"], d["eps"],
+                                     d["scale"], residual_out=ro, normed_fp8=q, fp8_scale=sc,
+                                     normed_out=no)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(10):
+        ro.fill_(0)
+        no.fill_(0)
+        q.view(torch.uint8).fill_(0)
+        sc.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.host_u16(ro), r0), i
+        assert np.array_equal(gu.host_u16(no), n0), i
+        assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q0), i
+        assert np.array_equal(sc.cpu().numpy().astype(np.float64), s0), i
