@@ -609,12 +609,14 @@ def summarize_trace(args):
     lines = [f"# rocprofv3 kernel trace: {args.title}", "",
              "Commands ($REPO is the repository root, $OUT any output directory):", "",
              "```", args.command, "```", "",
-             "| kernel | grid (threads) | workgroup | tokens | calls | avg µs | median µs | min µs | max µs |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             "| kernel | grid (threads) | workgroup | tokens | calls | avg µs | median µs | p10 µs | p90 µs | min µs | max µs |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
         short = name.replace("(mfr::Params)", "")
+        q = sorted(v)
+        p10, p90 = q[int(0.1 * (len(q) - 1))], q[int(0.9 * (len(q) - 1))]
         lines.append(f"| `{short}` | {grid} | {wg} | {grid // wg} | {len(v)} | {statistics.mean(v):.2f} | "
-                     f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+                     f"{statistics.median(v):.2f} | {p10:.2f} | {p90:.2f} | {min(v):.2f} | {max(v):.2f} |")
     if args.stats_csv:
         with open(args.stats_csv) as f:
             stats = f.read().strip()
