@@ -233,13 +233,22 @@ def cpu_baseline(d, min_seconds=10.0, max_passes=20):
     import synth
     nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     oracle.default()
-    t0 = time.perf_counter()
-    passes = 0
-    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
-        oracle.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
-                                d["residual"], d["gamma"], d["eps"], d["scale"], want_exact=False)
-        passes += 1
-    dt = time.perf_counter() - t0
+    # one core: the oracle is single-threaded; pinning keeps the scheduler
+    # from moving it between cores during the timed passes
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        t0 = time.perf_counter()
+        passes = 0
+        while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+            oracle.finalize_rmsnorm(d["expert_out"], d["perm_idx"], d["topk_w"], d["shared_out"],
+                                    d["residual"], d["gamma"], d["eps"], d["scale"],
+                                    want_exact=False)
+            passes += 1
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, allowed)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -251,9 +260,9 @@ def cpu_baseline(d, min_seconds=10.0, max_passes=20):
         pass
     return {"value": round(nbytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"the whole {d['T']}-token workload, {passes} passes, single thread "
-                      f"({dt:.1f} s; {dt / passes * 1e6:.0f} µs/call; host: {cpu}, "
-                      f"{os.cpu_count()} logical CPUs)"}
+            "sample": f"the whole {d['T']}-token workload, {passes} passes, single thread pinned to "
+                      f"core {core} ({dt:.1f} s; {dt / passes * 1e6:.0f} µs/call; host: {cpu}, "
+                      f"{len(allowed)} of {os.cpu_count()} logical CPUs available)"}
 
 
 def traffic_for_headline():
