@@ -305,6 +305,37 @@ def test_row_offsets_beyond_2gib():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
+def test_special_values_propagate(path):
+    """Inf and NaN inputs follow the definition on both sides. A token with
+    one infinite residual element gets Inf in residual_out there; its sum of
+    squares is infinite, so that element normalises to NaN (inf/inf) and the
+    others to +-0. A token with one NaN shared element gets NaN there in
+    residual_out, and its whole normed row is NaN. Other tokens are
+    untouched: special positions are compared exactly, finite values
+    through the gate."""
+    d = synth.generate(3, 2048, 8, scale=2.5, seed=31)
+    d["residual"] = d["residual"].copy()
+    d["shared_out"] = d["shared_out"].copy()
+    d["residual"][1, 5] = 0x7F80      # +inf
+    d["shared_out"][2, 7] = 0x7FC0    # NaN
+    dd = gu.to_device(d)
+    r, n = gu.run(dd, d["eps"], d["scale"], path=path)
+    ref = gu.oracle_for(d)
+    for got, want_exact, what in ((r, ref["s"], "residual_out"), (n, ref["normed_exact"], "normed_out")):
+        g = gu.bf16_f64(got)
+        assert np.array_equal(np.isnan(g), np.isnan(want_exact)), what
+        assert np.array_equal(np.isinf(g), np.isinf(want_exact)), what
+        assert np.array_equal(np.sign(g[np.isinf(g)]), np.sign(want_exact[np.isinf(want_exact)])), what
+        fin = np.isfinite(want_exact)
+        assert np.all(np.abs(g[fin] - want_exact[fin]) <= gu.REL * np.abs(want_exact[fin]) + gu.ABS), what
+    g_r, g_n = gu.bf16_f64(r), gu.bf16_f64(n)
+    assert np.isinf(g_r[1, 5]) and np.isnan(g_n[1, 5])
+    assert np.all(g_n[1, np.arange(2048) != 5] == 0.0)
+    assert np.isnan(g_r[2, 7]) and np.all(np.isnan(g_n[2]))
+    assert np.all(np.isfinite(g_r[0])) and np.all(np.isfinite(g_n[0]))
+
+
 def test_eps_zero_zero_row_is_nan():
     """eps = 0 and a token whose sum is exactly zero: 0/0 gives NaN in the
     normed output on both sides; residual_out is +-0."""
