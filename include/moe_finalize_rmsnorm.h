@@ -26,7 +26,9 @@
  *   bf16 tensors are passed as raw 16-bit patterns (uint16_t).
  *   expert_out   [R, H]  bf16   GEMM2 output rows; R is not passed. Every
  *                               non-negative perm_idx must be < R (not checked:
- *                               an index >= R reads out of bounds on the GPU).
+ *                               an index >= R reads out of bounds on the GPU;
+ *                               moe_finalize_rmsnorm_checked takes R and
+ *                               checks).
  *   perm_idx     [T, K]  int32  row of expert_out for (token t, slot k);
  *                               any negative value marks a masked slot, whose
  *                               row is never read and whose weight is ignored.
@@ -103,6 +105,27 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
                          float eps, float scale,
                          uint16_t* residual_out, uint16_t* normed_out,
                          int64_t T, int64_t H, int64_t K, hipStream_t stream);
+
+/* The fused op told the row count R of expert_out. A slot whose index is at
+ * or past R is treated as masked: its row is not read and its weight is
+ * ignored, so a wrong index cannot read outside expert_out. If bad_index is
+ * not NULL, the kernel sets *bad_index (int32, device memory, 4-byte
+ * aligned) to 1 when any token holds such an index. It never writes 0, so
+ * clear the flag before the call and read it after the stream has passed
+ * the kernel. The caller chooses between failing, retrying or accepting the
+ * masked result. R above 2^31 means the same as 2^31, because int32 indices
+ * address no more. With R known, the overlap check covers all of
+ * expert_out. Otherwise as moe_finalize_rmsnorm: for in-range indices the
+ * outputs are bit-identical to it. The operation is the one defined above
+ * (vLLM pull request #62174, Details). The row bound is this library's
+ * addition, for callers that cannot vouch for their indices. */
+int moe_finalize_rmsnorm_checked(const uint16_t* expert_out, int64_t R,
+                                 const int32_t* perm_idx, const float* topk_w,
+                                 const uint16_t* shared_out, const uint16_t* residual,
+                                 const uint16_t* gamma, float eps, float scale,
+                                 uint16_t* residual_out, uint16_t* normed_out,
+                                 int32_t* bad_index,
+                                 int64_t T, int64_t H, int64_t K, hipStream_t stream);
 
 /* The fused op with the normalised output also (or only) produced as dynamic
  * per-token FP8, the activation format of the FP8 projection that consumes it

@@ -82,6 +82,24 @@ int main() {
     expect(moe_finalize_rmsnorm(E, P, W, S, R, G, 1e-6f, 1.f, at<uint16_t>(A + 4 * step + 16), NO,
                                 T, H, K, nullptr), MFR_ERR_ALIAS, "residual_out overlaps residual");
 
+    // the op told R: its own checks, and the overlap check over all R rows
+    int32_t* FLAG = at<int32_t>(A + 10 * step);
+    expect(moe_finalize_rmsnorm_checked(E, -1, P, W, S, R, G, 1e-6f, 1.f, RO, NO, FLAG, T, H, K,
+                                        nullptr), MFR_ERR_SHAPE, "checked R < 0");
+    expect(moe_finalize_rmsnorm_checked(E, T * K, P, W, S, R, G, 1e-6f, 1.f, RO, NO, FLAG + 0, 0,
+                                        H, K, nullptr), MFR_OK, "checked T = 0");
+    expect(moe_finalize_rmsnorm_checked(nullptr, T * K, P, W, S, R, G, 1e-6f, 1.f, RO, NO, FLAG, T,
+                                        H, K, nullptr), MFR_ERR_NULL, "checked null rows");
+    expect(moe_finalize_rmsnorm_checked(E, T * K, P, W, S, R, G, 1e-6f, 1.f, RO, NO,
+                                        at<int32_t>(A + 10 * step + 2), T, H, K, nullptr),
+           MFR_ERR_ALIGN, "checked misaligned flag");
+    expect(moe_finalize_rmsnorm_checked(E, T * K, P, W, S, R, G, 1e-6f, 1.f, RO,
+                                        at<uint16_t>(A + 16 * H), FLAG, T, H, K, nullptr),
+           MFR_ERR_ALIAS, "checked output inside the rows");
+    expect(moe_finalize_rmsnorm_checked(E, (int64_t{1} << 40), P, W, S, R, G, 1e-6f, 1.f, RO, NO,
+                                        at<int32_t>(A + 3 * step), T, H, K, nullptr),
+           MFR_ERR_ALIAS, "checked huge R: the declared rows cover the outputs");
+
     // FP8 output
     expect(moe_finalize_rmsnorm_fp8(E, P, W, S, R, G, 1e-6f, 1.f, RO, nullptr, nullptr, SC, T, H, K,
                                     nullptr), MFR_ERR_NULL, "fp8 null codes");

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
                  "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force",
-                 "residual_add_rmsnorm", "moe_finalize_rmsnorm_fp8"):
+                 "residual_add_rmsnorm", "moe_finalize_rmsnorm_fp8",
+                 "moe_finalize_rmsnorm_checked"):
         assert want in names
 
 
@@ -245,3 +246,35 @@ def test_env_path_switch():
     assert _path_in_subprocess("stream", 8, forced=mfr.PATH_TOKEN)[0] == mfr.PATH_TOKEN
     p, err = _path_in_subprocess("fastest", 8)
     assert p == mfr.PATH_TOKEN and "MFR_PATH=fastest" in err
+
+
+def checked_call(R=T * K, bad_index=A + 71 * T * H * 2, T_=T, H_=H, K_=K, eps=1e-6, scale=2.5,
+                 **over):
+    p = _ptrs(**over)
+    return binding.lib().moe_finalize_rmsnorm_checked(
+        p["expert_out"], R, p["perm_idx"], p["topk_w"], p["shared_out"], p["residual"], p["gamma"],
+        eps, scale, p["residual_out"], p["normed_out"], bad_index, T_, H_, K_, None)
+
+
+def test_checked_validation():
+    """moe_finalize_rmsnorm_checked: the plain op's checks plus R and the
+    flag; with R known the overlap check covers all R rows of expert_out."""
+    act = T * H * 2
+    p = _ptrs()
+    assert checked_call(R=-1) == binding.MFR_ERR_SHAPE
+    assert checked_call(T_=T, H_=7) == binding.MFR_ERR_SHAPE
+    assert checked_call(eps=math.nan) == binding.MFR_ERR_SCALAR
+    assert checked_call(gamma=None) == binding.MFR_ERR_NULL
+    assert checked_call(expert_out=None) == binding.MFR_ERR_NULL  # R > 0 needs the rows
+    assert checked_call(bad_index=A + 71 * act + 2) == binding.MFR_ERR_ALIGN
+    assert checked_call(bad_index=p["normed_out"] + 8) == binding.MFR_ERR_ALIAS
+    assert checked_call(bad_index=p["perm_idx"]) == binding.MFR_ERR_ALIAS
+    # an output inside expert_out's R rows, past the first 16 bytes that the
+    # plain entry point (which is not told R) can check
+    inside = p["expert_out"] + (T * K // 2) * H * 2
+    assert checked_call(normed_out=inside) == binding.MFR_ERR_ALIAS
+    assert checked_call(residual_out=inside) == binding.MFR_ERR_ALIAS
+    # zero tokens: nothing examined, nothing launched
+    assert binding.lib().moe_finalize_rmsnorm_checked(None, 0, None, None, None, None, None, 1e-6,
+                                                      1.0, None, None, None, 0, H, K,
+                                                      None) == binding.MFR_OK

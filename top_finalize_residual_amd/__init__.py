@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     STORE_WRITE_BACK,
     STORE_WRITE_THROUGH,
     moe_finalize_rmsnorm,
+    moe_finalize_rmsnorm_checked,
     moe_finalize_rmsnorm_force,
     moe_finalize_rmsnorm_fp8,
     moe_finalize_rmsnorm_fp8_raw,

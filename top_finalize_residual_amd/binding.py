@@ -49,6 +49,9 @@ _lib.moe_finalize_rmsnorm_fp8.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_float
                                           _p, _p, _p, _p, _i64, _i64, _i64, _p]
 _lib.residual_add_rmsnorm.restype = ctypes.c_int
 _lib.residual_add_rmsnorm.argtypes = [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _p]
+_lib.moe_finalize_rmsnorm_checked.restype = ctypes.c_int
+_lib.moe_finalize_rmsnorm_checked.argtypes = [_p, _i64, _p, _p, _p, _p, _p, ctypes.c_float,
+                                              ctypes.c_float, _p, _p, _p, _i64, _i64, _i64, _p]
 _lib.moe_finalize_rmsnorm_force.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_force.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
 
@@ -161,6 +164,54 @@ def moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gam
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_out
+
+
+def moe_finalize_rmsnorm_checked(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
+                                 scale, residual_out=None, normed_out=None, bad_index=None,
+                                 stream=None):
+    """moe_finalize_rmsnorm told R = expert_out.shape[0]: a slot whose index
+    is at or past R is treated as masked instead of reading outside
+    expert_out, and bad_index (a one-element int32 GPU tensor, allocated
+    zeroed when not given) is set to 1 if any token holds such an index.
+    Returns (residual_out, normed_out, bad_index)."""
+    _check(expert_out, "expert_out", torch.bfloat16, 2)
+    _check(perm_idx, "perm_idx", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(shared_out, "shared_out", torch.bfloat16, 2)
+    _check(residual, "residual", torch.bfloat16, 2)
+    _check(gamma, "gamma", torch.bfloat16, 1)
+    T, K = perm_idx.shape
+    H = gamma.shape[0]
+    R = expert_out.shape[0]
+    if expert_out.shape[1] != H or tuple(shared_out.shape) != (T, H) or \
+            tuple(residual.shape) != (T, H) or tuple(topk_w.shape) != (T, K):
+        raise ValueError("inconsistent shapes")
+    dev = residual.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if normed_out is None:
+        normed_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if bad_index is None:
+        bad_index = torch.zeros((1,), dtype=torch.int32, device=dev)
+    _check(residual_out, "residual_out", torch.bfloat16, 2)
+    _check(normed_out, "normed_out", torch.bfloat16, 2)
+    _check(bad_index, "bad_index", torch.int32, 1)
+    if tuple(residual_out.shape) != (T, H) or tuple(normed_out.shape) != (T, H):
+        raise ValueError("outputs must be [T, H]")
+    if bad_index.numel() < 1:
+        raise ValueError("bad_index must hold one int32")
+    _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out,
+                 normed_out, bad_index)
+    stream, ctx = _launch_context(dev, stream)
+    with ctx:
+        rc = _lib.moe_finalize_rmsnorm_checked(
+            expert_out.data_ptr(), R, perm_idx.data_ptr(), topk_w.data_ptr(),
+            shared_out.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
+            float(scale), residual_out.data_ptr(), normed_out.data_ptr(), bad_index.data_ptr(),
+            T, H, K, stream.cuda_stream)
+    if rc != MFR_OK:
+        raise MFRError(rc)
+    return residual_out, normed_out, bad_index
 
 
 def residual_add_rmsnorm_raw(x, residual, gamma, eps, residual_out, normed_out, T, H, stream):

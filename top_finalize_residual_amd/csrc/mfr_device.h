@@ -75,6 +75,11 @@ __device__ __forceinline__ void buf_store_b32(float v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, AUX);
 }
 
+template <int AUX>
+__device__ __forceinline__ void buf_store_u32(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, AUX);
+}
+
 // 448 / m for m > 0, made safe to scale by: the correctly rounded quotient,
 // lowered by one ulp where m times it rounds above 448. Rounding is monotone,
 // so |x| <= m then gives |x * factor| <= 448 after rounding, the largest

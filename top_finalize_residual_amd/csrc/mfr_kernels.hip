@@ -67,6 +67,8 @@ struct Params {
     int K;
     uint8_t* normed_fp8;  // [T, H] E4M3 codes (FP8 output modes only)
     float* fp8_scale;     // [T] per-token scales (FP8 output modes only)
+    uint32_t rows;        // rows of expert_out, at most 2^31: an index at or past it is masked
+    int32_t* bad_index;   // optional: set to 1 when some slot's index is at or past R
 };
 
 // What the normalisation writes: the bf16 normed row, the per-token FP8
@@ -94,12 +96,16 @@ __device__ __forceinline__ void load_meta8(const Params& p, const int32_t* prow,
 
 // Loads the rows of slots [k0, k0 + 8) and folds them into acc in slot order.
 // Straight-line code: all eight row loads are issued, then the FMAs. A masked
-// slot (index < 0) or a slot at or past K gets a zero-record descriptor and a
-// zero weight: its loads return zeros without touching memory and its FMA
-// adds +0, which leaves acc bit-for-bit unchanged (acc starts at +0 and an
-// exact-zero sum rounds to +0). No branches.
-template <int VPT, bool CHECK_K>
-__device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&idx)[8],
+// slot (index < 0), a slot whose index is at or past R, or a slot at or past
+// K gets a zero-record descriptor and a zero weight: its loads return zeros
+// without touching memory and its FMA adds +0, which leaves acc bit-for-bit
+// unchanged (acc starts at +0 and an exact-zero sum rounds to +0). No
+// branches. ROWS (the entry point told R) also masks an index at or past
+// the rows and, when the caller asked for the report, returns whether a slot
+// within K held one (the indices are wave-uniform, so the result is too);
+// without ROWS the code is the plain index >= 0 test.
+template <int VPT, bool CHECK_K, bool ROWS>
+__device__ __forceinline__ bool gather_rows8(const Params& p, const int32_t (&idx)[8],
                                              const float (&wr)[8], int k0,
                                              const uint32_t (&off)[VPT], float (&acc)[VPT][8]) {
     const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
@@ -107,7 +113,10 @@ __device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&id
     float w[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-        const bool use = idx[kk] >= 0 && (!CHECK_K || k0 + kk < p.K);
+        // With ROWS, one unsigned compare masks both a negative index (it
+        // wraps to 2^31 or more) and one at or past the rows.
+        const bool in_range = ROWS ? static_cast<uint32_t>(idx[kk]) < p.rows : idx[kk] >= 0;
+        const bool use = in_range && (!CHECK_K || k0 + kk < p.K);
         rows[kk] = make_rsrc(p.expert_out + static_cast<int64_t>(use ? idx[kk] : 0) * p.V,
                              use ? rowbytes : 0u);
         const float ws = p.scale * wr[kk];
@@ -125,6 +134,16 @@ __device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&id
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 acc[j][e] = __builtin_fmaf(w[kk], vec_elem(r[kk][j], e), acc[j][e]);
+    // Whether a slot within K held an index at or past the rows: only asked
+    // for when the caller wants the report (a uniform branch).
+    bool past_r = false;
+    if (ROWS && p.bad_index != nullptr) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            past_r |= (!CHECK_K || k0 + kk < p.K) && idx[kk] >= 0 &&
+                      static_cast<uint32_t>(idx[kk]) >= p.rows;
+    }
+    return past_r;
 }
 
 // One token, end to end. KT: 8 = exactly eight slots (the GLM-5.x / DeepSeek
@@ -134,7 +153,7 @@ __device__ __forceinline__ void gather_rows8(const Params& p, const int32_t (&id
 // every row; offsets at or past the row end (a ragged last tile) fall outside
 // the descriptors' range, so their loads return zero and their stores are
 // dropped by the hardware.
-template <int VPT, int KT, int OUT_AUX, int QM>
+template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS>
 __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t, float* red) {
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
@@ -177,11 +196,16 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
         for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
 
     if constexpr (!DENSE) {
-        gather_rows8<VPT, CHECK_K>(p, idx, wr, 0, off, acc);
+        bool past_r = gather_rows8<VPT, CHECK_K, ROWS>(p, idx, wr, 0, off, acc);
         if (CHECK_K && p.K > 8) {
             load_meta8<true>(p, prow, wrow, 8, idx, wr);
-            gather_rows8<VPT, true>(p, idx, wr, 8, off, acc);
+            past_r |= gather_rows8<VPT, true, ROWS>(p, idx, wr, 8, off, acc);
         }
+        // Report an index past the rows (its slot was treated as masked).
+        // Every workgroup that sees one writes the same value, so there is
+        // no race on the result.
+        if (ROWS && past_r && p.bad_index != nullptr && tid == 0)
+            buf_store_u32<kAuxDefault>(1u, make_rsrc(p.bad_index, 4u), 0u);
     }
 
     // s = (routed + shared) + residual (dense: x + residual); residual_out =
@@ -318,11 +342,11 @@ struct Bound {
 // One workgroup per token. OUT_AUX is the cache policy of the output stores
 // (write-back, or write-through for outputs larger than the L2); QM the
 // OutMode of the normalised output.
-template <int VPT, int KT, int OUT_AUX, int QM>
+template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS = false>
 __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(Params p) {
     // Per-wave row sums and (FP8 modes) row maxima; 16-byte aligned for vector reads.
     __shared__ __align__(16) float red[2 * MAX_WAVES];
-    finalize_token<VPT, KT, OUT_AUX, QM>(p, static_cast<int64_t>(blockIdx.x), red);
+    finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(p, static_cast<int64_t>(blockIdx.x), red);
 }
 
 }  // namespace mfr
@@ -336,6 +360,9 @@ constexpr int64_t kHMax = 16384;
 constexpr int64_t kKMax = 16;
 constexpr int64_t kTMax = 2147483647;
 constexpr int kVptMax = 4;
+// Row bound of the entry points that are not told R: 2^31, above every
+// non-negative int32 index, so no slot is ever treated as past the rows.
+constexpr uint32_t kNoRowBound = 0x80000000u;
 // Token counts up to this use the token path (widest workgroup per token).
 // Measured on MI355X at H = 6144: the token path is ahead up to T = 256, the
 // 256-thread stream shape from T = 512.
@@ -420,21 +447,26 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-template <int VPT, int KT, int QM>
+template <int VPT, int KT, int QM, bool ROWS = false>
 const void* pick_store(bool wt) {
     return wt ? reinterpret_cast<const void*>(
-                    &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough, QM>)
-              : reinterpret_cast<const void*>(&mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut, QM>);
+                    &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough, QM, ROWS>)
+              : reinterpret_cast<const void*>(
+                    &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut, QM, ROWS>);
 }
 
-// Routing variant of a launch: exactly eight slots, any K, or no routed part.
-enum Variant { kTop8 = 8, kAnyK = 0, kDense = -1 };
+// Routing variant of a launch: exactly eight slots, any K, or no routed part;
+// the checked forms also bound the indices by the rows of expert_out.
+enum Variant { kTop8 = 8, kAnyK = 0, kDense = -1, kTop8Rows = 108, kAnyKRows = 100 };
 
 template <int VPT, int QM>
 const void* pick_variant(Variant v, bool wt) {
     switch (v) {
         case kTop8: return pick_store<VPT, 8, QM>(wt);
         case kAnyK: return pick_store<VPT, 0, QM>(wt);
+        // the checked forms exist for the bf16 output only
+        case kTop8Rows: return pick_store<VPT, 8, mfr::kOutBf16, true>(wt);
+        case kAnyKRows: return pick_store<VPT, 0, mfr::kOutBf16, true>(wt);
         default: return pick_store<VPT, -1, QM>(wt);
     }
 }
@@ -497,7 +529,8 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
                      "moe_finalize_rmsnorm: T=%lld H=%lld K=%d variant=%s out=%s path=%s vpt=%d "
                      "threads=%d stores=%s\n",
                      static_cast<long long>(T), static_cast<long long>(H), p.K,
-                     v == kTop8 ? "top8" : v == kAnyK ? "anyK" : "dense",
+                     v == kTop8 ? "top8" : v == kAnyK ? "anyK" : v == kTop8Rows ? "top8-rows" :
+                     v == kAnyKRows ? "anyK-rows" : "dense",
                      qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16",
                      path == MFR_PATH_TOKEN ? "token" : "stream", vpt, nt,
                      wt ? "write-through" : "write-back");
@@ -550,7 +583,53 @@ int moe_finalize_rmsnorm(const uint16_t* expert_out, const int32_t* perm_idx,
     p.eps = eps;
     p.scale = scale;
     p.K = static_cast<int>(K);
+    p.rows = kNoRowBound;
     return launch(p, T, H, K == 8 ? kTop8 : kAnyK, mfr::kOutBf16, stream);
+}
+
+int moe_finalize_rmsnorm_checked(const uint16_t* expert_out, int64_t R, const int32_t* perm_idx,
+                                 const float* topk_w, const uint16_t* shared_out,
+                                 const uint16_t* residual, const uint16_t* gamma, float eps,
+                                 float scale, uint16_t* residual_out, uint16_t* normed_out,
+                                 int32_t* bad_index, int64_t T, int64_t H, int64_t K,
+                                 hipStream_t stream) {
+    if (!shape_ok(T, H, K) || R < 0) return MFR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(scale)) return MFR_ERR_SCALAR;
+    if (T == 0) return MFR_OK;
+    // int32 indices address at most 2^31 rows: a larger R means the same.
+    if (R > (int64_t{1} << 31)) R = int64_t{1} << 31;
+    if (!perm_idx || !topk_w || !shared_out || !residual || !gamma || !residual_out ||
+        !normed_out || (R > 0 && !expert_out))
+        return MFR_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(shared_out, 16) || !aligned(residual, 16) ||
+        !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(normed_out, 16) ||
+        !aligned(perm_idx, 4) || !aligned(topk_w, 4) || (bad_index && !aligned(bad_index, 4)))
+        return MFR_ERR_ALIGN;
+    const uint64_t act = static_cast<uint64_t>(T) * H * 2;
+    const uint64_t meta = static_cast<uint64_t>(T) * K * 4;
+    // With R known, the whole of expert_out takes part in the overlap check.
+    const Extent outs[] = {{residual_out, act}, {normed_out, act}, {bad_index, bad_index ? 4u : 0u}};
+    const Extent ins[] = {{residual, act}, {shared_out, act}, {gamma, static_cast<uint64_t>(H) * 2},
+                          {perm_idx, meta}, {topk_w, meta},
+                          {expert_out, static_cast<uint64_t>(R) * static_cast<uint64_t>(H) * 2}};
+    const int rc = check_aliasing(outs, 3, ins, 6, residual_out, residual);
+    if (rc != MFR_OK) return rc;
+
+    mfr::Params p = {};
+    p.expert_out = reinterpret_cast<const mfr::u32x4*>(expert_out);
+    p.perm_idx = perm_idx;
+    p.topk_w = topk_w;
+    p.shared_out = reinterpret_cast<const mfr::u32x4*>(shared_out);
+    p.residual = reinterpret_cast<const mfr::u32x4*>(residual);
+    p.gamma = reinterpret_cast<const mfr::u32x4*>(gamma);
+    p.residual_out = reinterpret_cast<mfr::u32x4*>(residual_out);
+    p.normed_out = reinterpret_cast<mfr::u32x4*>(normed_out);
+    p.eps = eps;
+    p.scale = scale;
+    p.K = static_cast<int>(K);
+    p.rows = static_cast<uint32_t>(R);
+    p.bad_index = bad_index;
+    return launch(p, T, H, K == 8 ? kTop8Rows : kAnyKRows, mfr::kOutBf16, stream);
 }
 
 int moe_finalize_rmsnorm_fp8(const uint16_t* expert_out, const int32_t* perm_idx,
@@ -595,6 +674,7 @@ int moe_finalize_rmsnorm_fp8(const uint16_t* expert_out, const int32_t* perm_idx
     p.eps = eps;
     p.scale = scale;
     p.K = static_cast<int>(K);
+    p.rows = kNoRowBound;
     return launch(p, T, H, K == 8 ? kTop8 : kAnyK, normed_out ? mfr::kOutBoth : mfr::kOutFp8,
                   stream);
 }
@@ -624,6 +704,7 @@ int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint
     p.eps = eps;
     p.scale = 1.0f;
     p.K = 0;
+    p.rows = kNoRowBound;
     return launch(p, T, H, kDense, mfr::kOutBf16, stream);
 }
 
