@@ -27,6 +27,8 @@ int main(void) {
                                  NULL, NULL, 0, 2048, 8, NULL) != MFR_OK) bad |= 32;
     if (moe_finalize_rmsnorm_force(MFR_PATH_STREAM + 1, 0, 0) != MFR_ERR_ARG) bad |= 64;
     if (strlen(moe_finalize_rmsnorm_strerror(MFR_ERR_ALIAS)) == 0) bad |= 128;
+    if (moe_finalize_rmsnorm_checked(NULL, -1, NULL, NULL, NULL, NULL, NULL, 1e-6f, 1.0f, NULL,
+                                     NULL, NULL, 4, 2048, 8, NULL) != MFR_ERR_SHAPE) bad |= 256;
     printf("%d\n", bad);
     return bad;
 }
