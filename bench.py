@@ -168,7 +168,7 @@ def _probe_lib():
     lib.mfr_write_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int,
                                     ctypes.c_void_p]
     lib.mfr_empty_probe.restype = ctypes.c_int
-    lib.mfr_empty_probe.argtypes = [ctypes.c_void_p]
+    lib.mfr_empty_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -210,14 +210,15 @@ def probe_ceilings(nbytes=1 << 30, reps=10):
     return best["copy"], best["read"], best["write"]
 
 
-def launch_floor_us():
-    """Per-launch device µs of an empty kernel inside a graph of 100 launches:
-    the floor under any kernel measured the way decode_latency measures."""
+def launch_floor_us(grid=1, threads=64):
+    """Per-launch device µs of an empty kernel (grid workgroups of `threads`)
+    inside a graph of 100 launches: the floor under any kernel of that launch
+    shape, measured the way decode_latency measures."""
     import torch
     lib = _probe_lib()
 
     def empty():
-        if lib.mfr_empty_probe(torch.cuda.current_stream().cuda_stream) != 0:
+        if lib.mfr_empty_probe(grid, threads, torch.cuda.current_stream().cuda_stream) != 0:
             raise RuntimeError("empty probe failed")
     return round(time_graph([empty], 100, 5) * 1e3, 2)
 
@@ -387,8 +388,11 @@ def decode_latency(cold_bytes=600_000_000):
                 same[f"T{T}"], fresh[f"T{T}"] = a, b
             else:
                 variants[f"{mode}_T{T}"] = {"same_inputs": a, "fresh_inputs": b}
+    # the floor under each decode launch: an empty kernel of the token
+    # path's launch shape (T workgroups of 768 threads at H = 6144)
+    floor = {f"T{T}": launch_floor_us(T, 768) for T in DECODE_TS}
     return {"same_inputs": same, "fresh_inputs": fresh, **variants,
-            "empty_kernel_floor": launch_floor_us()}
+            "empty_kernel_floor": floor}
 
 
 def graph_ceiling_batch():

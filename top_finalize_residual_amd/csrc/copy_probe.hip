@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void mfr_write_probe_kernel(u32x4* __rest
 }
 
 // Does nothing: its launch-to-completion time is the floor under any kernel.
-__global__ void mfr_empty_probe_kernel() {}
+__global__ __launch_bounds__(1024) void mfr_empty_probe_kernel() {}
 
 // Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) on
 // `stream` with `grid` workgroups of 256 threads. Returns 0 on success, 1 on
@@ -128,9 +128,11 @@ extern "C" int mfr_write_probe(void* dst, int64_t bytes, uint32_t pattern, int g
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// Launches the empty kernel with one workgroup of 64 threads. Returns 0 on
-// success, 2 if the launch failed.
-extern "C" int mfr_empty_probe(hipStream_t stream) {
-    hipLaunchKernelGGL(mfr_empty_probe_kernel, dim3(1), dim3(64), 0, stream);
+// Launches the empty kernel with `grid` workgroups of `threads` threads (at
+// most 1024). Returns 0 on success, 1 on bad arguments, 2 if the launch
+// failed.
+extern "C" int mfr_empty_probe(int grid, int threads, hipStream_t stream) {
+    if (grid <= 0 || threads <= 0 || threads > 1024) return 1;
+    hipLaunchKernelGGL(mfr_empty_probe_kernel, dim3(grid), dim3(threads), 0, stream);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
