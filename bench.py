@@ -666,8 +666,7 @@ def summarize_pmc(args):
     cf = copy_bytes / (f_copy * 1024.0)
     cw = copy_bytes / (w_copy * 1024.0)
     import synth
-    d = synth.config_inputs(HEADLINE_CFG, HEADLINE_T)
-    alg = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    alg = synth.config_algorithmic_bytes(HEADLINE_CFG, HEADLINE_T)
     traffic = f_fused * 1024.0 * cf + w_fused * 1024.0 * cw
     out = {"kernel": fk, "code_hash": kernel_code_hash(),
            "fetch_kib_per_dispatch": f_fused, "write_kib_per_dispatch": w_fused,

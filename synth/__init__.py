@@ -197,6 +197,16 @@ def config_inputs(cfg, T=None):
                     mask_frac=c["mask_frac"], spike_frac=c["spike_frac"], seed=seed_for(cfg, T))
 
 
+def config_algorithmic_bytes(cfg, T):
+    """algorithmic_bytes of a named workload with no masked slots, without
+    drawing its inputs (every slot is valid: T * K gathered rows)."""
+    c = CONFIGS[cfg]
+    if c["mask_frac"] != 0.0:
+        raise ValueError(f"{cfg} masks slots: count them with algorithmic_bytes")
+    H, K = c["H"], c["K"]
+    return 2 * H * T * K + 4 * (2 * H) * T + 8 * K * T + 2 * H
+
+
 def algorithmic_bytes(perm_idx, H, K):
     """Bytes the op must move: valid gathered rows, shared, residual, both
     outputs (2H bytes each per token), the K index and K weight entries per

@@ -1,0 +1,108 @@
+"""Host logic of bench.py that the committed profiles come from, on synthetic
+rocprofv3 CSVs with known answers (CPU only): the kernel-trace summary
+(mean, median, p10, p90), the FETCH_SIZE / WRITE_SIZE calibration against
+the 1 GiB copy probe, the code-hash gate on roofline.traffic, and the byte
+count of the headline workload."""
+import argparse
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _args(**kw):
+    base = dict(summarize_trace=None, kernel_filter="mfr_", stats_csv="", title="t", command="c",
+                out=None, fetch_csv=None, write_csv=None)
+    base.update(kw)
+    return argparse.Namespace(**base)
+
+
+def test_trace_summary_statistics(tmp_path):
+    trace = tmp_path / "kernel_trace.csv"
+    durations_us = [float(v) for v in range(1, 101)]  # 1..100 µs
+    with open(trace, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp",
+                    "End_Timestamp"])
+        t = 0
+        for d in durations_us:
+            w.writerow(["void mfr::mfr_fused_kernel<3, 8, 16, 0, false>(mfr::Params)", 2048, 256,
+                        t, t + int(d * 1000)])
+            t += 10 ** 6
+        w.writerow(["__amd_rocclr_copyBuffer", 1, 1, 0, 5000])  # filtered out
+    stats = tmp_path / "kernel_stats.csv"
+    stats.write_text('"Name","Calls"\n"x",1\n')
+    out = tmp_path / "summary.md"
+    bench.summarize_trace(_args(summarize_trace=str(trace), stats_csv=str(stats), out=str(out)))
+    text = out.read_text()
+    row = [ln for ln in text.splitlines() if ln.startswith("| `void mfr::")]
+    assert len(row) == 1 and "copyBuffer" not in row[0]
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    # kernel, grid, workgroup, tokens, calls, avg, median, p10, p90, min, max
+    assert cells[1:5] == ["2048", "256", "8", "100"]
+    assert cells[5:] == ["50.50", "50.50", "10.00", "90.00", "1.00", "100.00"]
+    assert '"Name","Calls"' in text  # the stats table is appended verbatim
+
+
+def _pmc_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+        for name, value in rows:
+            w.writerow([name, counter, value])
+
+
+def test_pmc_calibration(tmp_path, monkeypatch):
+    """The copy probe moves exactly 1 GiB each way; the counters it reads
+    give the scale factors for the fused kernel's counters."""
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    fused = "void mfr::mfr_fused_kernel<3, 8, 16, 0, false>(mfr::Params)"
+    copy = "mfr_copy_probe_kernel(u32x4 const*, u32x4*, long)"
+    _pmc_csv(fetch, "FETCH_SIZE", [(fused, 500000.0), (fused, 500002.0), (copy, 524288.0)])
+    _pmc_csv(write, "WRITE_SIZE", [(fused, 196608.0), (copy, 1048576.0)])
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda: "abc")
+    out = tmp_path / "traffic.json"
+    bench.summarize_pmc(_args(fetch_csv=str(fetch), write_csv=str(write), out=str(out)))
+    t = json.loads(out.read_text())
+    assert t["copy_probe"]["fetch_scale"] == 2.0 and t["copy_probe"]["write_scale"] == 1.0
+    assert t["fetch_kib_per_dispatch"] == 500001.0
+    assert t["traffic_bytes_per_launch"] == round(500001.0 * 1024 * 2 + 196608.0 * 1024)
+    assert t["algorithmic_bytes"] == 1208496128 and t["code_hash"] == "abc"
+
+
+def test_traffic_gate_follows_the_code_hash(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"code_hash": "h1", "traffic_bytes_per_launch": 123}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda: "h1")
+    assert bench.traffic_for_headline() == 123
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda: "h2")
+    assert bench.traffic_for_headline() is None
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda: None)
+    assert bench.traffic_for_headline() is None
+
+
+def test_code_hash_reads_the_embedded_code_objects(tmp_path):
+    from top_finalize_residual_amd import build as b
+    if not os.path.exists(b.LIB):
+        pytest.skip("HIP library not built")
+    sec = bench._elf_section(b.LIB, ".hip_fatbin")
+    assert sec is not None and len(sec) > 0
+    assert bench.kernel_code_hash() == bench.kernel_code_hash()
+    not_elf = tmp_path / "x.so"
+    not_elf.write_bytes(b"not an ELF file")
+    assert bench._elf_section(str(not_elf), ".hip_fatbin") is None
+
+
+def test_closed_form_bytes_match_drawn_inputs():
+    d = synth.config_inputs("batch512", 512)
+    assert synth.config_algorithmic_bytes("batch512", 512) == synth.algorithmic_bytes(
+        d["perm_idx"], d["H"], d["K"])
+    with pytest.raises(ValueError):
+        synth.config_algorithmic_bytes("decode_masked", 4)
