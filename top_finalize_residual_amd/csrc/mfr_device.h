@@ -80,6 +80,17 @@ __device__ __forceinline__ void buf_store_u32(uint32_t v, rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, AUX);
 }
 
+// 1 / sqrt(x) for x >= 0 through the hardware v_rsq_f32 (within 1 ulp; the
+// fp32 sum of squares feeding it already carries several). That instruction
+// treats a subnormal input as zero, so inputs below 2^-100 are scaled by 2^64
+// first and the result by 2^32 after, both exact. x = 0 gives +inf, +inf
+// gives 0, NaN stays NaN.
+__device__ __forceinline__ float rsqrt_f32(float x) {
+    const bool tiny = x < 0x1p-100f;
+    const float r = __builtin_amdgcn_rsqf(tiny ? x * 0x1p64f : x);
+    return tiny ? r * 0x1p32f : r;
+}
+
 // 448 / m for m > 0, made safe to scale by: the correctly rounded quotient,
 // lowered by one ulp where m times it rounds above 448. Rounding is monotone,
 // so |x| <= m then gives |x * factor| <= 448 after rounding, the largest

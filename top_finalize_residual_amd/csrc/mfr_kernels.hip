@@ -268,7 +268,7 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     float rmg = 0.0f;
 #pragma unroll
     for (int w = MAX_WAVES; w < NRED; ++w) rmg = __builtin_fmaxf(rmg, part[w]);
-    const float rstd = 1.0f / __builtin_sqrtf(tot / p.h_f + p.eps);
+    const float rstd = rsqrt_f32(tot / p.h_f + p.eps);
 
     if (QM != kOutFp8) {
         const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
