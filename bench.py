@@ -20,6 +20,8 @@ Modes used with rocprofv3 (see profiles/):
                      dense op at T=28 and 8192), to trace
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
+  --summarize-counters  join shader and L2 counter passes (occupancy, VALU busy,
+                     instructions per wave, LDS bank conflicts, L2 hit rate)
 """
 import argparse
 import csv
@@ -679,6 +681,86 @@ def summarize_pmc(args):
     print(json.dumps(out, indent=1))
 
 
+# Shader-engine counters gathered in three rocprofv3 --pmc passes (each within
+# one pass's per-block limits); the summary joins them per kernel launch shape.
+COUNTER_PASSES = (
+    ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS",
+     "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_SALU"),
+    ("TCC_HIT_sum", "TCC_MISS_sum"),
+    ("VALUBusy", "OccupancyPercent"),
+)
+
+
+def summarize_counters(args):
+    """Per (kernel, grid, workgroup): the mean of each counter over its
+    dispatches, from any number of rocprofv3 counter_collection.csv files.
+    Derived here: L2 hit rate = hits / (hits + misses), and instructions per
+    wave. VALUBusy and OccupancyPercent are rocprofv3's own derived counters."""
+    groups = {}
+    for path in args.counter_csv:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if args.kernel_filter and args.kernel_filter not in name:
+                continue
+            key = (name.split("(")[0].replace("void ", ""), int(r["Grid_Size"]),
+                   int(r["Workgroup_Size"]))
+            g = groups.setdefault(key, {"vgpr": r["VGPR_Count"], "sgpr": r["SGPR_Count"],
+                                        "lds": r["LDS_Block_Size"], "c": {}})
+            g["c"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+
+    def mean(g, c):
+        v = g["c"].get(c)
+        return sum(v) / len(v) if v else None
+
+    def fmt(x, nd=1):
+        return "—" if x is None else f"{x:,.{nd}f}"
+    rows, out = [], {}
+    for (name, grid, wg), g in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        waves = mean(g, "SQ_WAVES")
+        hit, miss = mean(g, "TCC_HIT_sum"), mean(g, "TCC_MISS_sum")
+        l2 = 100.0 * hit / (hit + miss) if hit is not None and miss is not None and hit + miss > 0 else None
+
+        def per_wave(c):
+            v = mean(g, c)
+            return v / waves if v is not None and waves else None
+        n_disp = max(len(v) for v in g["c"].values())
+        rec = {"dispatches": n_disp, "waves": waves, "vgpr": int(g["vgpr"]), "sgpr": int(g["sgpr"]),
+               "lds_bytes": int(g["lds"]), "occupancy_pct": mean(g, "OccupancyPercent"),
+               "valu_busy_pct": mean(g, "VALUBusy"), "valu_per_wave": per_wave("SQ_INSTS_VALU"),
+               "salu_per_wave": per_wave("SQ_INSTS_SALU"),
+               "vmem_rd_per_wave": per_wave("SQ_INSTS_VMEM_RD"),
+               "vmem_wr_per_wave": per_wave("SQ_INSTS_VMEM_WR"), "lds_per_wave": per_wave("SQ_INSTS_LDS"),
+               "lds_bank_conflict": mean(g, "SQ_LDS_BANK_CONFLICT"),
+               "l2_hit_pct": l2,
+               "l2_hit": hit, "l2_miss": miss}
+        out[f"{name} grid={grid} wg={wg}"] = rec
+        rows.append(f"| `{name}` | {grid // wg} × {wg} | {n_disp} | {rec['vgpr']} / {rec['sgpr']} / "
+                    f"{rec['lds_bytes']} | {fmt(waves, 0)} | {fmt(rec['occupancy_pct'])} | "
+                    f"{fmt(rec['valu_busy_pct'])} | {fmt(rec['valu_per_wave'])} | "
+                    f"{fmt(rec['salu_per_wave'])} | {fmt(rec['vmem_rd_per_wave'])} | "
+                    f"{fmt(rec['vmem_wr_per_wave'])} | {fmt(rec['lds_per_wave'])} | "
+                    f"{fmt(rec['lds_bank_conflict'], 0)} | {fmt(l2)} |")
+    lines = [f"# rocprofv3 counters: {args.title}", "",
+             "Commands ($REPO is the repository root, $OUT any output directory):", "",
+             "```", args.command, "```", "",
+             "Per launch shape, means over its dispatches. VGPR / SGPR / LDS are rocprofv3's columns "
+             "(LDS in bytes); on gfx950 its VGPR figure is half the compiler's allocation (143 registers "
+             "show as 72), so waves per SIMD follow from the compiler's count. Occupancy and VALU busy are rocprofv3's derived `OccupancyPercent` "
+             "and `VALUBusy`; per-wave columns are instruction counts divided by `SQ_WAVES`; the LDS "
+             "column is `SQ_LDS_BANK_CONFLICT` per dispatch; L2 hit = `TCC_HIT_sum` / (`TCC_HIT_sum` + "
+             "`TCC_MISS_sum`).", "",
+             "| kernel | workgroups × threads | dispatches | VGPR / SGPR / LDS | waves | occupancy % | "
+             "VALU busy % | VALU / wave | SALU / wave | VMEM rd / wave | VMEM wr / wave | LDS / wave | "
+             "LDS bank conflict | L2 hit % |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"] + rows
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            json.dump(out, f, indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -696,12 +778,18 @@ def main():
     ap.add_argument("--stats-csv", default="", help="with --summarize-trace: append this kernel_stats.csv")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
+    ap.add_argument("--summarize-counters", action="store_true")
+    ap.add_argument("--counter-csv", action="append", default=[],
+                    help="with --summarize-counters: a counter_collection.csv (repeatable)")
+    ap.add_argument("--json-out", default="", help="with --summarize-counters: also write JSON")
     ap.add_argument("--out")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the fused op has no cross-GPU step to time here "

@@ -1,7 +1,7 @@
 """Host logic of bench.py that the committed profiles come from, on synthetic
 rocprofv3 CSVs with known answers (CPU only): the kernel-trace summary
 (mean, median, p10, p90), the FETCH_SIZE / WRITE_SIZE calibration against
-the 1 GiB copy probe, the code-hash gate on roofline.traffic, and the byte
+the 1 GiB copy probe, the join of the shader and L2 counter passes, the code-hash gate on roofline.traffic, and the byte
 count of the headline workload."""
 import argparse
 import csv
@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _args(**kw):
     base = dict(summarize_trace=None, kernel_filter="mfr_", stats_csv="", title="t", command="c",
-                out=None, fetch_csv=None, write_csv=None)
+                out=None, fetch_csv=None, write_csv=None, counter_csv=[], json_out="")
     base.update(kw)
     return argparse.Namespace(**base)
 
@@ -105,3 +105,49 @@ def test_closed_form_bytes_match_drawn_inputs():
         d["perm_idx"], d["H"], d["K"])
     with pytest.raises(ValueError):
         synth.config_algorithmic_bytes("decode_masked", 4)
+
+
+def test_counter_summary_joins_passes(tmp_path):
+    """Three passes over two dispatches of one launch shape and one of
+    another: means per shape, instructions per wave, and the L2 hit rate."""
+    cols = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "VGPR_Count", "SGPR_Count",
+            "LDS_Block_Size", "Counter_Name", "Counter_Value"]
+    fused = "void mfr::mfr_fused_kernel<3, 8, 16, 0, false>(mfr::Params)"
+    small = "void mfr::mfr_fused_kernel<1, 8, 0, 0, false>(mfr::Params)"
+    passes = [
+        [(fused, 2048, 256, "SQ_WAVES", 32), (fused, 2048, 256, "SQ_INSTS_VALU", 3200),
+         (fused, 2048, 256, "SQ_LDS_BANK_CONFLICT", 0),
+         (fused, 2048, 256, "SQ_WAVES", 32), (fused, 2048, 256, "SQ_INSTS_VALU", 3840),
+         (fused, 2048, 256, "SQ_LDS_BANK_CONFLICT", 10),
+         (small, 768, 768, "SQ_WAVES", 12), (small, 768, 768, "SQ_INSTS_VALU", 1200),
+         ("__amd_rocclr_copyBuffer", 64, 64, "SQ_WAVES", 1)],
+        [(fused, 2048, 256, "TCC_HIT_sum", 30), (fused, 2048, 256, "TCC_MISS_sum", 70),
+         (fused, 2048, 256, "TCC_HIT_sum", 10), (fused, 2048, 256, "TCC_MISS_sum", 90)],
+        [(fused, 2048, 256, "OccupancyPercent", 40.0), (fused, 2048, 256, "OccupancyPercent", 60.0),
+         (fused, 2048, 256, "VALUBusy", 5.0), (fused, 2048, 256, "VALUBusy", 7.0)],
+    ]
+    paths = []
+    for i, rows in enumerate(passes):
+        p = tmp_path / f"pass{i}.csv"
+        with open(p, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(cols)
+            for name, grid, wg, c, v in rows:
+                w.writerow([name, grid, wg, 72, 64, 512, c, v])
+        paths.append(str(p))
+    out, js = tmp_path / "c.md", tmp_path / "c.json"
+    bench.summarize_counters(_args(counter_csv=paths, out=str(out), json_out=str(js)))
+    rec = json.loads(js.read_text())
+    assert len(rec) == 2  # the copy kernel is filtered out
+    big = rec["mfr::mfr_fused_kernel<3, 8, 16, 0, false> grid=2048 wg=256"]
+    assert big["dispatches"] == 2 and big["waves"] == 32
+    assert big["valu_per_wave"] == pytest.approx(3520 / 32)
+    assert big["lds_bank_conflict"] == 5
+    assert big["l2_hit_pct"] == pytest.approx(20.0)
+    assert big["occupancy_pct"] == 50.0 and big["valu_busy_pct"] == 6.0
+    assert (big["vgpr"], big["sgpr"], big["lds_bytes"]) == (72, 64, 512)
+    tiny = rec["mfr::mfr_fused_kernel<1, 8, 0, 0, false> grid=768 wg=768"]
+    assert tiny["valu_per_wave"] == 100 and tiny["l2_hit_pct"] is None
+    text = out.read_text()
+    assert "| `mfr::mfr_fused_kernel<3, 8, 16, 0, false>` | 8 × 256 | 2 |" in text
+    assert "| `mfr::mfr_fused_kernel<1, 8, 0, 0, false>` | 1 × 768 | 1 |" in text
