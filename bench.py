@@ -20,6 +20,9 @@ Modes used with rocprofv3 (see profiles/):
                      dense op at T=28 and 8192), to trace
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
+  --pmc-variants-run the dense tail and the FP8-output call at T=8192, plus the
+                     copy probe, for the same two counters
+  --summarize-pmc-variants  their calibrated traffic against their own bytes
   --summarize-counters  join shader and L2 counter passes (occupancy, VALU busy,
                      instructions per wave, LDS bank conflicts, L2 hit rate)
 """
@@ -611,6 +614,29 @@ def run_pmc(args):
     log("pmc run done")
 
 
+def run_pmc_variants(args):
+    """Short run for counter collection on the 8192-token chunk: the dense
+    residual add + RMSNorm, the FP8-output call, then one 1 GiB copy of known
+    size."""
+    import torch
+    import synth
+    torch.cuda.set_device(0)
+    T = HEADLINE_T
+    dense = make_dense_caller(synth.dense_inputs(T, 6144, seed=synth.seed_for(HEADLINE_CFG, T),
+                                                 spike_frac=0.01))
+    for _ in range(args.steps):
+        dense()
+    torch.cuda.synchronize()
+    del dense
+    fp8 = stacked_calls(synth.config_inputs(HEADLINE_CFG, T), 1, "fp8")[0]
+    for _ in range(args.steps):
+        fp8()
+    torch.cuda.synchronize()
+    del fp8
+    probe_ceilings(reps=1)
+    log("pmc variants run done")
+
+
 def summarize_trace(args):
     """Per (kernel, grid, workgroup) durations from a rocprofv3 kernel_trace.csv."""
     import statistics
@@ -679,6 +705,73 @@ def summarize_pmc(args):
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def _fused_template_args(name):
+    """(VPT, KT, OUT_AUX, QM, ROWS) of an mfr_fused_kernel name, as strings."""
+    inside = name[name.index("<") + 1:name.index(">")]
+    return tuple(a.strip() for a in inside.split(","))
+
+
+def variant_algorithmic_bytes(name, T=HEADLINE_T):
+    """Closed-form algorithmic bytes of one launch of a fused-kernel variant on
+    the T-token prefill chunk: the dense tail (KT = -1), the FP8-output modes
+    (QM 1: codes and scale, QM 2: also the bf16 normed output), else the
+    bf16 fused op."""
+    import synth
+    _, kt, _, qm, _ = _fused_template_args(name)
+    if kt == "-1":
+        if qm != "0":
+            raise ValueError(f"no byte count for the dense FP8 variant {name}")
+        return synth.dense_algorithmic_bytes(T, synth.CONFIGS[HEADLINE_CFG]["H"])
+    if qm in ("1", "2"):
+        return synth.config_fp8_algorithmic_bytes(HEADLINE_CFG, T, bf16_normed=qm == "2")
+    return synth.config_algorithmic_bytes(HEADLINE_CFG, T)
+
+
+def summarize_pmc_variants(args):
+    """FETCH_SIZE and WRITE_SIZE of every fused-kernel variant in the run,
+    calibrated on the copy probe of the same run, against each variant's
+    algorithmic bytes."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+    fetch = per_kernel(args.fetch_csv, "FETCH_SIZE")
+    write = per_kernel(args.write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "mfr_copy_probe_kernel" in k]
+    if not copy or copy[0] not in write:
+        raise SystemExit("no copy probe in the counter files")
+    copy_bytes = 1 << 30
+    cf = copy_bytes / (fetch[copy[0]] * 1024.0)
+    cw = copy_bytes / (write[copy[0]] * 1024.0)
+    rows, out = [], {"code_hash": kernel_code_hash(), "fetch_scale": cf, "write_scale": cw,
+                     "kernels": {}, "commands": args.command}
+    for name in sorted(k for k in fetch if "mfr_fused_kernel" in k and k in write):
+        short = name.split("(")[0].replace("void ", "")
+        alg = variant_algorithmic_bytes(name)
+        traffic = fetch[name] * 1024.0 * cf + write[name] * 1024.0 * cw
+        out["kernels"][short] = {"fetch_kib": fetch[name], "write_kib": write[name],
+                                 "traffic_bytes": round(traffic), "algorithmic_bytes": alg,
+                                 "ratio": traffic / alg}
+        rows.append(f"| `{short}` | {fetch[name]:,.0f} | {write[name]:,.0f} | {traffic:,.0f} | "
+                    f"{alg:,} | {traffic / alg:.4f} |")
+    lines = [f"# HBM traffic: {args.title}", "",
+             "Commands ($REPO is the repository root, $OUT any output directory):", "",
+             "```", args.command, "```", "",
+             f"Calibration on the 1 GiB copy probe of the same run: FETCH_SIZE x {cf:.4f}, "
+             f"WRITE_SIZE x {cw:.4f}. Traffic = calibrated fetch + write bytes per dispatch; "
+             "the ratio is traffic over the variant's algorithmic bytes.", "",
+             "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | traffic B | "
+             "algorithmic B | ratio |", "|---|---|---|---|---|---|"] + rows
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            json.dump(out, f, indent=1)
+    print("\n".join(lines))
 
 
 # Shader-engine counters gathered in three rocprofv3 --pmc passes (each within
@@ -778,6 +871,8 @@ def main():
     ap.add_argument("--stats-csv", default="", help="with --summarize-trace: append this kernel_stats.csv")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
+    ap.add_argument("--pmc-variants-run", action="store_true")
+    ap.add_argument("--summarize-pmc-variants", action="store_true")
     ap.add_argument("--summarize-counters", action="store_true")
     ap.add_argument("--counter-csv", action="append", default=[],
                     help="with --summarize-counters: a counter_collection.csv (repeatable)")
@@ -790,6 +885,8 @@ def main():
         return summarize_pmc(args)
     if args.summarize_counters:
         return summarize_counters(args)
+    if args.summarize_pmc_variants:
+        return summarize_pmc_variants(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the fused op has no cross-GPU step to time here "
@@ -798,6 +895,8 @@ def main():
         sys.exit(2)
     if args.pmc_run:
         return run_pmc(args)
+    if args.pmc_variants_run:
+        return run_pmc_variants(args)
     if args.latency_run:
         return run_latency(args)
     return run_bench(args)

@@ -207,6 +207,17 @@ def config_algorithmic_bytes(cfg, T):
     return 2 * H * T * K + 4 * (2 * H) * T + 8 * K * T + 2 * H
 
 
+def config_fp8_algorithmic_bytes(cfg, T, bf16_normed=False):
+    """fp8_algorithmic_bytes of a named workload with no masked slots, without
+    drawing its inputs."""
+    c = CONFIGS[cfg]
+    if c["mask_frac"] != 0.0:
+        raise ValueError(f"{cfg} masks slots: count them with fp8_algorithmic_bytes")
+    H, K = c["H"], c["K"]
+    per_token_out = 2 * H + H + 4 + (2 * H if bf16_normed else 0)
+    return 2 * H * T * K + 2 * (2 * H) * T + 8 * K * T + 2 * H + per_token_out * T
+
+
 def algorithmic_bytes(perm_idx, H, K):
     """Bytes the op must move: valid gathered rows, shared, residual, both
     outputs (2H bytes each per token), the K index and K weight entries per

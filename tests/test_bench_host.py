@@ -105,6 +105,48 @@ def test_closed_form_bytes_match_drawn_inputs():
         d["perm_idx"], d["H"], d["K"])
     with pytest.raises(ValueError):
         synth.config_algorithmic_bytes("decode_masked", 4)
+    for normed in (False, True):
+        assert synth.config_fp8_algorithmic_bytes("batch512", 512, normed) == \
+            synth.fp8_algorithmic_bytes(d["perm_idx"], d["H"], d["K"], bf16_normed=normed)
+    with pytest.raises(ValueError):
+        synth.config_fp8_algorithmic_bytes("decode_masked", 4)
+
+
+def test_variant_bytes_follow_the_template_arguments():
+    T, H, K = 8192, 6144, 8
+    assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, -1, 16, 0, false>(x)") == \
+        8 * H * T + 2 * H
+    # FP8 codes only: reads as the fused op, residual_out, codes and one scale per token
+    assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, 8, 16, 1, false>(x)") == \
+        2 * H * T * K + 4 * H * T + 8 * K * T + 2 * H + (2 * H + H + 4) * T
+    assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, 8, 16, 2, false>(x)") == \
+        2 * H * T * K + 4 * H * T + 8 * K * T + 2 * H + (4 * H + H + 4) * T
+    assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, 8, 16, 0, false>(x)") == \
+        1208496128
+    with pytest.raises(ValueError):
+        bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, -1, 16, 1, false>(x)")
+
+
+def test_pmc_variants_calibration(tmp_path, monkeypatch):
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    dense = "void mfr::mfr_fused_kernel<3, -1, 16, 0, false>(mfr::Params)"
+    fp8 = "void mfr::mfr_fused_kernel<3, 8, 16, 1, false>(mfr::Params)"
+    copy = "mfr_copy_probe_kernel(u32x4 const*, u32x4*, long)"
+    _pmc_csv(fetch, "FETCH_SIZE", [(dense, 100000.0), (dense, 100002.0), (fp8, 490000.0),
+                                   (copy, 524288.0)])
+    _pmc_csv(write, "WRITE_SIZE", [(dense, 196608.0), (fp8, 147456.0), (copy, 1048576.0)])
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda: "abc")
+    out, js = tmp_path / "v.md", tmp_path / "v.json"
+    bench.summarize_pmc_variants(_args(fetch_csv=str(fetch), write_csv=str(write), out=str(out),
+                                       json_out=str(js)))
+    t = json.loads(js.read_text())
+    assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0 and t["code_hash"] == "abc"
+    k = t["kernels"]["mfr::mfr_fused_kernel<3, -1, 16, 0, false>"]
+    assert k["traffic_bytes"] == round(100001.0 * 1024 * 2 + 196608.0 * 1024)
+    assert k["ratio"] == pytest.approx(k["traffic_bytes"] / (8 * 6144 * 8192 + 2 * 6144))
+    assert set(t["kernels"]) == {"mfr::mfr_fused_kernel<3, -1, 16, 0, false>",
+                                 "mfr::mfr_fused_kernel<3, 8, 16, 1, false>"}
+    assert out.read_text().count("| `mfr::mfr_fused_kernel<") == 2
 
 
 def test_counter_summary_joins_passes(tmp_path):
