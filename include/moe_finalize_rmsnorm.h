@@ -48,6 +48,10 @@
  *
  * Limits: 0 <= T <= 2^31-1, 8 <= H <= 16384 with H % 8 == 0, 1 <= K <= 16.
  * bf16 pointers must be 16-byte aligned; perm_idx and topk_w 4-byte aligned.
+ * One workgroup serves one token, and a dispatch holds fewer than 2^32
+ * work-items: a call whose T times the workgroup size (64 to 1024 threads)
+ * reaches that is enqueued as several dispatches in stream order, with the
+ * same results.
  *
  * Ownership and ordering: the caller owns every buffer; the library allocates
  * and frees nothing and keeps no per-call state (on the page, releasing the
@@ -60,7 +64,8 @@
  * Errors: every argument check runs on the host before anything is enqueued.
  * On error nothing is launched and a nonzero status is returned; no exception
  * crosses the ABI. T == 0 returns MFR_OK without launching (pointers are then
- * not examined). A failed launch returns MFR_ERR_HIP.
+ * not examined). A failed launch returns MFR_ERR_HIP; if it was not the first
+ * dispatch of a split call, the dispatches before it stay enqueued.
  */
 #ifndef MOE_FINALIZE_RMSNORM_H
 #define MOE_FINALIZE_RMSNORM_H

@@ -514,7 +514,36 @@ int check_aliasing(const Extent* outs, int n_out, const Extent* ins, int n_in,
     return MFR_OK;
 }
 
-// Fills the shape fields, picks the launch shape and enqueues the kernel.
+// The work-item count of one dispatch (workgroups x threads per workgroup) is
+// a 32-bit quantity on this hardware, so a launch of T workgroups of nt
+// threads holds at most this many tokens; more are split over several
+// dispatches.
+int64_t tokens_per_dispatch(int nt) {
+    return static_cast<int64_t>(0xFFFFFFFFu / static_cast<uint32_t>(nt));
+}
+
+// p with every per-token pointer moved to token t0, so that a dispatch whose
+// workgroup 0 is token t0 addresses the same bytes as workgroup t0 of one
+// undivided grid. expert_out (addressed through the indices), gamma and the
+// report flag are shared by all tokens and stay as they are.
+mfr::Params from_token(const mfr::Params& p, int64_t t0) {
+    mfr::Params q = p;
+    const int64_t vec = t0 * p.V;  // 16-byte vectors before token t0 in a [T, H] bf16 tensor
+    if (p.perm_idx) q.perm_idx = p.perm_idx + t0 * p.K;
+    if (p.topk_w) q.topk_w = p.topk_w + t0 * p.K;
+    q.shared_out = p.shared_out + vec;
+    q.residual = p.residual + vec;
+    q.residual_out = p.residual_out + vec;
+    if (p.normed_out) q.normed_out = p.normed_out + vec;
+    if (p.normed_fp8) q.normed_fp8 = p.normed_fp8 + vec * 8;  // one byte per element
+    if (p.fp8_scale) q.fp8_scale = p.fp8_scale + t0;
+    return q;
+}
+
+// Fills the shape fields, picks the launch shape and enqueues the kernel: one
+// dispatch, or several in stream order when T x threads needs more than 32
+// bits. Every token's arithmetic is the same in any dispatch, so the split
+// changes no result.
 int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t stream) {
     p.T = T;
     p.h_f = static_cast<float>(H);
@@ -524,20 +553,27 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     const int nt = threads_for(p.V, vpt);
     const bool wt = write_through(path, T, H);
     const void* kern = kernel_for(vpt, v, wt, qm);
+    const int64_t per = tokens_per_dispatch(nt);
     if (g_env_log)
         std::fprintf(stderr,
                      "moe_finalize_rmsnorm: T=%lld H=%lld K=%d variant=%s out=%s path=%s vpt=%d "
-                     "threads=%d stores=%s\n",
+                     "threads=%d stores=%s dispatches=%lld\n",
                      static_cast<long long>(T), static_cast<long long>(H), p.K,
                      v == kTop8 ? "top8" : v == kAnyK ? "anyK" : v == kTop8Rows ? "top8-rows" :
                      v == kAnyKRows ? "anyK-rows" : "dense",
                      qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16",
                      path == MFR_PATH_TOKEN ? "token" : "stream", vpt, nt,
-                     wt ? "write-through" : "write-back");
-    void* args[] = {&p};
-    const hipError_t e =
-        hipLaunchKernel(kern, dim3(static_cast<uint32_t>(T)), dim3(nt), args, 0, stream);
-    return e == hipSuccess ? MFR_OK : MFR_ERR_HIP;
+                     wt ? "write-through" : "write-back", static_cast<long long>((T + per - 1) / per));
+    for (int64_t t0 = 0; t0 < T; t0 += per) {
+        const int64_t n = T - t0 < per ? T - t0 : per;
+        mfr::Params q = t0 == 0 ? p : from_token(p, t0);
+        q.T = n;
+        void* args[] = {&q};
+        const hipError_t e =
+            hipLaunchKernel(kern, dim3(static_cast<uint32_t>(n)), dim3(nt), args, 0, stream);
+        if (e != hipSuccess) return MFR_ERR_HIP;
+    }
+    return MFR_OK;
 }
 
 }  // namespace
