@@ -11,7 +11,8 @@ timed region; HIP events on the launch stream bracket exactly --steps calls.
 Printed (stdout, one JSON line): effective HBM GB/s = algorithmic bytes per
 call / time per call, the roofline object for the fused kernel, the oracle's
 CPU baseline on the same workload, and, as context, decode-latency figures for
-T = 1..64 and the 512-token batch, plus a measured copy ceiling.
+T = 1..64 and the 512-token batch, a measured copy ceiling, and the headline
+workload with its gathered rows grouped by expert instead of randomly placed.
 
 Modes used with rocprofv3 (see profiles/):
   --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
@@ -483,6 +484,33 @@ def fp8_figures():
                               "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}}
 
 
+def layout_figures(d, warmup=6, steps=60):
+    """The headline workload in two row layouts, interleaved A/B/B/A: the
+    uniformly random permutation the headline uses, and the rows grouped by
+    expert as a grouped GEMM2 writes them (every value a token gathers is the
+    same; only where the rows sit differs)."""
+    import numpy as np
+    import synth
+    nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    sorted_perm = synth.expert_sorted_perm(d["experts"])
+    moved = np.empty_like(d["expert_out"])
+    moved[sorted_perm.reshape(-1)] = d["expert_out"][d["perm_idx"].reshape(-1)]
+    ds = dict(d, expert_out=moved, perm_idx=sorted_perm)
+    calls = {"random": make_caller(to_device(d), d["eps"], d["scale"])[0],
+             "expert_sorted": make_caller(to_device(ds), d["eps"], d["scale"])[0]}
+    us = {"random": [], "expert_sorted": []}
+    for order in (("random", "expert_sorted"), ("expert_sorted", "random")):
+        for n in order:
+            us[n].append(time_calls([calls[n]], steps, warmup) * 1e3)
+    return {"prefill_T8192": {n: _rate(sum(v) / len(v), nbytes) for n, v in us.items()}}
+
+
+def _rate(us, nbytes):
+    """µs per call, GB/s and fraction of the HBM peak for nbytes per call."""
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def deferred_overhead():
     """Host cost of the torch-facing deferred path at one decode step (T=28):
     eager calls through fused_add_rmsnorm (custom op dispatch + ctypes) and
@@ -590,6 +618,8 @@ def run_bench(args):
         rec["dense_residual_rmsnorm"] = dense_figures()
         log("FP8 (E4M3 per-token) normalised output")
         rec["fp8_output"] = fp8_figures()
+        log("row layouts: random permutation against rows grouped by expert")
+        rec["row_layouts"] = layout_figures(d)
         log("deferred-finalize torch path: host overhead")
         rec["deferred_path"] = deferred_overhead()
     if not args.no_cpu_baseline:

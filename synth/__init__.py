@@ -93,13 +93,30 @@ def _softmax64(logits):
     return e / e.sum(axis=1, keepdims=True)
 
 
+def expert_sorted_perm(experts):
+    """perm_idx [T, K] of the expert-sorted row layout, from the expert each
+    (token, slot) picked: a pair's row is its rank when the pairs are sorted
+    by expert, ties (one expert, several tokens) in token order."""
+    experts = np.asarray(experts)
+    n = experts.size
+    by_expert = np.argsort(experts.reshape(-1), kind="stable")
+    flat = np.empty(n, dtype=np.int32)
+    flat[by_expert] = np.arange(n, dtype=np.int32)
+    return flat.reshape(experts.shape)
+
+
 def generate(T, H, K, *, scale=2.5, eps=EPS, weights="softmax_k", mask_frac=0.0,
-             spike_frac=0.0, seed=BASE_SEED, extra_rows=0):
+             spike_frac=0.0, seed=BASE_SEED, extra_rows=0, layout="random"):
     """Draw one input set.
 
     weights: "softmax_k"   - softmax over the K slots of N(0,1) logits;
              "top8_of_256" - softmax over the K largest of 256 N(0,1) logits
                              (ties go to the lower expert index).
+    layout: "random"        - the rows of expert_out in a uniformly random order;
+            "expert_sorted" - grouped by the expert each (token, slot) picked,
+                              tokens in order within an expert: the layout of a
+                              grouped GEMM2 output (needs "top8_of_256"; every
+                              other array is the same as with "random").
     mask_frac: fraction of (token, slot) pairs masked, rounded up; masked pairs get
                perm_idx = -1 and weight 0, and each token's remaining weights are
                renormalised to sum to 1 (an all-masked token keeps zero weights).
@@ -114,6 +131,7 @@ def generate(T, H, K, *, scale=2.5, eps=EPS, weights="softmax_k", mask_frac=0.0,
     expert_out = _normal_bf16(rng["expert_out"], (R, H), 0.0, 1.0)
     perm = rng["perm"].permutation(T * K).astype(np.int32).reshape(T, K)
 
+    order = None
     if weights == "softmax_k":
         logits = rng["logits"].standard_normal((T, K), dtype=np.float32)
         w64 = _softmax64(logits)
@@ -126,6 +144,12 @@ def generate(T, H, K, *, scale=2.5, eps=EPS, weights="softmax_k", mask_frac=0.0,
         w64 = _softmax64(np.take_along_axis(logits, order, axis=1))
     else:
         raise ValueError(f"unknown weights recipe {weights!r}")
+    if layout == "expert_sorted":
+        if weights != "top8_of_256":
+            raise ValueError("the expert_sorted layout needs the experts of top8_of_256")
+        perm = expert_sorted_perm(order)
+    elif layout != "random":
+        raise ValueError(f"unknown layout {layout!r}")
 
     if mask_frac > 0 and T * K > 0:
         m = int(math.ceil(mask_frac * T * K))
@@ -161,7 +185,8 @@ def generate(T, H, K, *, scale=2.5, eps=EPS, weights="softmax_k", mask_frac=0.0,
 
     return dict(expert_out=expert_out, perm_idx=perm, topk_w=topk_w, shared_out=shared,
                 residual=resid, gamma=gamma, eps=float(np.float32(eps)),
-                scale=float(np.float32(scale)), T=T, H=H, K=K, R=R, spike_rows=spike_rows)
+                scale=float(np.float32(scale)), T=T, H=H, K=K, R=R, spike_rows=spike_rows,
+                experts=None if order is None else order.astype(np.int32))
 
 
 def dense_inputs(T, H, *, eps=EPS, seed=BASE_SEED, spike_frac=0.0):

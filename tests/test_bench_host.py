@@ -193,3 +193,9 @@ def test_counter_summary_joins_passes(tmp_path):
     text = out.read_text()
     assert "| `mfr::mfr_fused_kernel<3, 8, 16, 0, false>` | 8 × 256 | 2 |" in text
     assert "| `mfr::mfr_fused_kernel<1, 8, 0, 0, false>` | 1 × 768 | 1 |" in text
+
+
+def test_rate_units():
+    # 1,208,496,128 bytes in 195 µs is 6197.4 GB/s, 77.47% of 8 TB/s
+    r = bench._rate(195.0, 1208496128)
+    assert r == {"us": 195.0, "gbs": 6197.4, "frac": 0.7747}

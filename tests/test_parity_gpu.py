@@ -56,6 +56,24 @@ def test_store_policies(cfg_data, path, store):
     gu.check(d, r, n, ref=ref)
 
 
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_expert_sorted_layout(path):
+    """The rows of expert_out grouped by expert, as a grouped GEMM2 writes
+    them (the layout the bench also times), against the oracle; and the same
+    tokens through the random layout give the same outputs bit for bit, since
+    each token gathers the same values either way."""
+    kw = dict(scale=2.5, weights="top8_of_256", seed=synth.seed_for("batch512", 512))
+    d = synth.generate(512, 6144, 8, layout="expert_sorted", **kw)
+    dr = synth.generate(512, 6144, 8, **kw)
+    # same values per (token, slot): rearrange the random layout's rows into this one
+    moved = dict(dr, expert_out=np.empty_like(dr["expert_out"]), perm_idx=d["perm_idx"])
+    moved["expert_out"][d["perm_idx"].reshape(-1)] = dr["expert_out"][dr["perm_idx"].reshape(-1)]
+    r, n = gu.run(gu.to_device(moved), d["eps"], d["scale"], path=path)
+    gu.check(moved, r, n)
+    r2, n2 = gu.run(gu.to_device(dr), d["eps"], d["scale"], path=path)
+    assert np.array_equal(r, r2) and np.array_equal(n, n2)
+
+
 def test_prefill_chunk_full_size_sampled():
     """The 8192-token prefill chunk at full size in the default (benchmarked)
     launch configuration; the oracle checks every spiked row plus a seeded
