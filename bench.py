@@ -21,8 +21,9 @@ Modes used with rocprofv3 (see profiles/):
                      dense op at T=28 and 8192), to trace
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
-  --pmc-variants-run the dense tail and the FP8-output call at T=8192, plus the
-                     copy probe, for the same two counters
+  --pmc-variants-run the dense tail, the FP8-output call and the dense tail with
+                     FP8 output at T=8192, plus the copy probe, for the same
+                     two counters
   --summarize-pmc-variants  their calibrated traffic against their own bytes
   --summarize-counters  join shader and L2 counter passes (occupancy, VALU busy,
                      instructions per wave, LDS bank conflicts, L2 hit rate)
@@ -452,6 +453,38 @@ def dense_figures():
                               "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}}
 
 
+def _dense_fp8_caller(d):
+    """A zero-allocation closure: one dense residual add + RMSNorm with FP8
+    output (codes and scales, no bf16 normed output) on its own device copy."""
+    import torch
+    import top_finalize_residual_amd as mfr
+    T, H = d["T"], d["H"]
+    x, res, g = (torch.from_numpy(d[k].view("int16")).view(torch.bfloat16).cuda()
+                 for k in ("x", "residual", "gamma"))
+    ro = torch.empty_like(res)
+    q = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((T,), dtype=torch.float32, device="cuda")
+
+    def call():
+        _raise_on(mfr.residual_add_rmsnorm_fp8_raw(
+            x.data_ptr(), res.data_ptr(), g.data_ptr(), d["eps"], ro.data_ptr(), None,
+            q.data_ptr(), sc.data_ptr(), T, H, torch.cuda.current_stream().cuda_stream))
+    call.keep = (x, res, g, ro, q, sc)
+    return call
+
+
+def dense_fp8_figures():
+    """The dense residual add + RMSNorm with its normalised output as per-token
+    FP8 (no bf16 normed output) on the 8192-token chunk, HBM-cold (3 rotating
+    buffer sets)."""
+    import synth
+    T, H = 8192, 6144
+    d = synth.dense_inputs(T, H, seed=synth.seed_for("prefill", T), spike_frac=0.01)
+    ms = time_calls([_dense_fp8_caller(d) for _ in range(3)], 60, 6)
+    return {"prefill_T8192": dict(_rate(ms * 1e3, synth.dense_fp8_algorithmic_bytes(T, H)),
+                                  bytes=synth.dense_fp8_algorithmic_bytes(T, H))}
+
+
 def fp8_figures():
     """The fused op with its normalised output as per-token FP8 (no bf16 normed
     output) on the 8192-token chunk (HBM-cold by size)."""
@@ -618,6 +651,8 @@ def run_bench(args):
         rec["dense_residual_rmsnorm"] = dense_figures()
         log("FP8 (E4M3 per-token) normalised output")
         rec["fp8_output"] = fp8_figures()
+        log("dense residual add + RMSNorm with FP8 output")
+        rec["dense_fp8_output"] = dense_fp8_figures()
         log("row layouts: random permutation against rows grouped by expert")
         rec["row_layouts"] = layout_figures(d)
         log("deferred-finalize torch path: host overhead")
@@ -663,6 +698,12 @@ def run_pmc_variants(args):
         fp8()
     torch.cuda.synchronize()
     del fp8
+    dense_fp8 = _dense_fp8_caller(synth.dense_inputs(T, 6144, seed=synth.seed_for(HEADLINE_CFG, T),
+                                                     spike_frac=0.01))
+    for _ in range(args.steps):
+        dense_fp8()
+    torch.cuda.synchronize()
+    del dense_fp8
     probe_ceilings(reps=1)
     log("pmc variants run done")
 
@@ -750,10 +791,11 @@ def variant_algorithmic_bytes(name, T=HEADLINE_T):
     bf16 fused op."""
     import synth
     _, kt, _, qm, _ = _fused_template_args(name)
+    H = synth.CONFIGS[HEADLINE_CFG]["H"]
     if kt == "-1":
-        if qm != "0":
-            raise ValueError(f"no byte count for the dense FP8 variant {name}")
-        return synth.dense_algorithmic_bytes(T, synth.CONFIGS[HEADLINE_CFG]["H"])
+        if qm in ("1", "2"):
+            return synth.dense_fp8_algorithmic_bytes(T, H, bf16_normed=qm == "2")
+        return synth.dense_algorithmic_bytes(T, H)
     if qm in ("1", "2"):
         return synth.config_fp8_algorithmic_bytes(HEADLINE_CFG, T, bf16_normed=qm == "2")
     return synth.config_algorithmic_bytes(HEADLINE_CFG, T)

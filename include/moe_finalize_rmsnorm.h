@@ -180,6 +180,24 @@ int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint
                          float eps, uint16_t* residual_out, uint16_t* normed_out,
                          int64_t T, int64_t H, hipStream_t stream);
 
+/* The dense residual add + RMSNorm with the normalised output also (or only)
+ * produced as dynamic per-token FP8, for a dense tail whose output feeds an
+ * FP8 projection (the page's attention projections take dynamic per-token
+ * activation scales: "Port the validated GLM-5.2 H200 production path to
+ * latest vLLM", Prepared experiment branches). The FP8 rule is the one of
+ * moe_finalize_rmsnorm_fp8, applied to the fp32 normalised row of
+ * residual_add_rmsnorm. Arguments as for residual_add_rmsnorm, plus:
+ *   normed_out   [T, H] bf16   optional: NULL skips the bf16 normed output
+ *   normed_fp8   [T, H] uint8  E4M3 codes, 8-byte aligned
+ *   fp8_scale    [T]    fp32   per-token scale, 4-byte aligned
+ * No output may overlap another output or any input (residual_out ==
+ * residual excepted). residual_out, and normed_out when given, are
+ * bit-identical to those of residual_add_rmsnorm with the same arguments. */
+int residual_add_rmsnorm_fp8(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                             float eps, uint16_t* residual_out, uint16_t* normed_out,
+                             uint8_t* normed_fp8, float* fp8_scale,
+                             int64_t T, int64_t H, hipStream_t stream);
+
 /* Which path moe_finalize_rmsnorm would take for this shape, taking any
  * override from moe_finalize_rmsnorm_force into account; MFR_PATH_UNSUPPORTED
  * if the shape is outside the limits. Pure host function: no HIP call. A

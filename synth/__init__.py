@@ -213,6 +213,14 @@ def dense_algorithmic_bytes(T, H):
     return 8 * H * T + 2 * H
 
 
+def dense_fp8_algorithmic_bytes(T, H, bf16_normed=False):
+    """The dense tail writing its normalised output as FP8: x, residual and
+    residual_out (2H bytes each per token), the E4M3 codes (H) and the scale
+    (4) per token, the bf16 normed output (2H) when it is also written, plus
+    gamma once."""
+    return (6 * H + H + 4 + (2 * H if bf16_normed else 0)) * T + 2 * H
+
+
 def config_inputs(cfg, T=None):
     """Inputs of a named workload config at token count T (default: its first T)."""
     c = CONFIGS[cfg]

@@ -119,6 +119,19 @@ int main() {
            "dense outputs alias");
     expect(residual_add_rmsnorm(S, R, G, 1e-6f, RO, NO, 0, H, nullptr), MFR_OK, "dense T = 0");
 
+    // dense tail with FP8 output
+    expect(residual_add_rmsnorm_fp8(S, R, G, 1e-6f, RO, nullptr, nullptr, SC, T, H, nullptr),
+           MFR_ERR_NULL, "dense fp8 null codes");
+    expect(residual_add_rmsnorm_fp8(S, R, G, 1e-6f, RO, nullptr, Q + 4, SC, T, H, nullptr),
+           MFR_ERR_ALIGN, "dense fp8 misaligned codes");
+    expect(residual_add_rmsnorm_fp8(S, R, G, -1.f, RO, nullptr, Q, SC, T, H, nullptr),
+           MFR_ERR_SCALAR, "dense fp8 eps");
+    expect(residual_add_rmsnorm_fp8(S, R, G, 1e-6f, RO, NO, reinterpret_cast<uint8_t*>(NO), SC, T,
+                                    H, nullptr),
+           MFR_ERR_ALIAS, "dense fp8 codes on the bf16 normed output");
+    expect(residual_add_rmsnorm_fp8(S, R, G, 1e-6f, RO, NO, Q, SC, 0, H, nullptr), MFR_OK,
+           "dense fp8 T = 0");
+
     if (failures) return 1;
     std::printf("abi driver: ok\n");
     return 0;

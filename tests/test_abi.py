@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
                  "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force",
                  "residual_add_rmsnorm", "moe_finalize_rmsnorm_fp8",
-                 "moe_finalize_rmsnorm_checked"):
+                 "moe_finalize_rmsnorm_checked", "residual_add_rmsnorm_fp8"):
         assert want in names
 
 
@@ -212,6 +212,40 @@ def test_fp8_validation():
     assert fp8_call(normed_out=base["normed_fp8"]) == binding.MFR_ERR_ALIAS
     # without the optional bf16 output, its pointer is not examined
     assert fp8_call(T_=0, normed_out=None) == binding.MFR_OK
+
+
+def dense_fp8_call(T_=T, H_=H, eps=1e-6, **over):
+    act = T * H * 2
+    p = dict(x=A, residual=A + 4 * act, gamma=A + 8 * act, residual_out=A + 12 * act,
+             normed_out=A + 16 * act, normed_fp8=A + 20 * act, fp8_scale=A + 24 * act)
+    p.update(over)
+    return mfr.residual_add_rmsnorm_fp8_raw(p["x"], p["residual"], p["gamma"], eps,
+                                            p["residual_out"], p["normed_out"], p["normed_fp8"],
+                                            p["fp8_scale"], T_, H_, None)
+
+
+def test_dense_fp8_validation():
+    act = T * H * 2
+    for name in ("x", "residual", "gamma", "residual_out", "normed_fp8", "fp8_scale"):
+        assert dense_fp8_call(**{name: None}) == binding.MFR_ERR_NULL, name
+    for name in ("x", "residual", "gamma", "residual_out", "normed_out"):
+        assert dense_fp8_call(**{name: A + 30 * act + 8}) == binding.MFR_ERR_ALIGN, name
+    assert dense_fp8_call(normed_fp8=A + 20 * act + 4) == binding.MFR_ERR_ALIGN
+    assert dense_fp8_call(fp8_scale=A + 24 * act + 2) == binding.MFR_ERR_ALIGN
+    for shape in ((-1, H), (T, 0), (T, 12), (T, 16392), (2**31, H)):
+        assert dense_fp8_call(*shape) == binding.MFR_ERR_SHAPE, shape
+    for eps in (-1.0, math.nan, math.inf):
+        assert dense_fp8_call(eps=eps) == binding.MFR_ERR_SCALAR
+    # codes on the residual output, the scale inside the codes, codes on an input,
+    # the bf16 normed output on the codes
+    assert dense_fp8_call(normed_fp8=A + 12 * act) == binding.MFR_ERR_ALIAS
+    assert dense_fp8_call(fp8_scale=A + 20 * act + 64) == binding.MFR_ERR_ALIAS
+    assert dense_fp8_call(normed_fp8=A) == binding.MFR_ERR_ALIAS
+    assert dense_fp8_call(normed_out=A + 20 * act) == binding.MFR_ERR_ALIAS
+    # without the optional bf16 output, its pointer is not examined
+    assert dense_fp8_call(T_=0, normed_out=None) == binding.MFR_OK
+    assert mfr.residual_add_rmsnorm_fp8_raw(None, None, None, 1e-6, None, None, None, None, 0, H,
+                                            None) == binding.MFR_OK
 
 
 def _path_in_subprocess(env_value, T, forced=0):

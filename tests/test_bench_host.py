@@ -123,8 +123,11 @@ def test_variant_bytes_follow_the_template_arguments():
         2 * H * T * K + 4 * H * T + 8 * K * T + 2 * H + (4 * H + H + 4) * T
     assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, 8, 16, 0, false>(x)") == \
         1208496128
-    with pytest.raises(ValueError):
-        bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, -1, 16, 1, false>(x)")
+    # dense FP8: x, residual, residual_out, codes and one scale per token
+    assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, -1, 16, 1, false>(x)") == \
+        (6 * H + H + 4) * T + 2 * H
+    assert bench.variant_algorithmic_bytes("void mfr::mfr_fused_kernel<3, -1, 16, 2, false>(x)") == \
+        (8 * H + H + 4) * T + 2 * H
 
 
 def test_pmc_variants_calibration(tmp_path, monkeypatch):

@@ -46,6 +46,33 @@ def test_custom_ops_are_registered_with_fake_kernels():
         assert r is x
 
 
+def test_fp8_consumer_ops_with_fake_tensors():
+    from torch._subclasses.fake_tensor import FakeTensorMode
+    for name in ("moe_finalize_rmsnorm_fp8", "moe_finalize_rmsnorm_fp8_",
+                 "residual_add_rmsnorm_fp8", "residual_add_rmsnorm_fp8_"):
+        assert hasattr(torch.ops.mfr, name), name
+    with FakeTensorMode():
+        x = torch.empty(4, 64, dtype=torch.bfloat16)
+        g = torch.empty(64, dtype=torch.bfloat16)
+        r, q, sc = mfr.fused_add_rmsnorm(x, torch.empty_like(x), g, 1e-6, fp8=True)
+        assert r.shape == (4, 64) and q.shape == (4, 64) and q.dtype == torch.float8_e4m3fn
+        assert sc.shape == (4,) and sc.dtype == torch.float32
+        u = mfr.UnfinalizedMoEOutput(torch.empty(32, 64, dtype=torch.bfloat16),
+                                     torch.zeros(4, 8, dtype=torch.int32), torch.zeros(4, 8))
+        res = torch.empty_like(x)
+        out = mfr.fused_add_rmsnorm(mfr.MoEOutput(u, x), res, g, 1e-6, fp8=True, in_place=True)
+        assert out[0] is res and len(out) == 3
+
+
+def test_fp8_consumer_argument_rules():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="not normed_out"):
+        mfr.fused_add_rmsnorm(x, x.clone(), g, 1e-6, fp8=True, normed_out=torch.empty_like(x))
+    with pytest.raises(ValueError, match="outputs of fp8=True"):
+        mfr.fused_add_rmsnorm(x, x.clone(), g, 1e-6, fp8_scale=torch.empty(4))
+
+
 def test_cpu_tensors_are_refused():
     # the product path has no CPU fallback
     x = torch.zeros(4, 64, dtype=torch.bfloat16)

@@ -138,3 +138,56 @@ def test_decoder_tail_graph_replay():
         torch.cuda.synchronize()
         assert np.array_equal(gu.host_u16(res_g), want_res), i
         assert np.array_equal(gu.host_u16(h_g), want_h), i
+
+
+@pytest.mark.parametrize("in_place", [False, True], ids=["separate", "in_place"])
+@pytest.mark.parametrize("deferred", [True, False], ids=["moe", "dense"])
+def test_fp8_consumer_equals_direct_calls(deferred, in_place):
+    """fused_add_rmsnorm(fp8=True): the residual stream, codes and scales
+    bit-identical to the direct FP8 calls, for a deferred MoEOutput (fused
+    kernel) and a plain tensor (dense kernel), in place or not."""
+    d = synth.generate(28, 6144, 8, scale=2.5, mask_frac=0.05, seed=68)
+    dd, u = _dev(d)
+    if deferred:
+        hidden = mfr.MoEOutput(u, dd["shared_out"])
+        r0, q0, s0, _ = mfr.moe_finalize_rmsnorm_fp8(dd["expert_out"], dd["perm_idx"],
+                                                     dd["topk_w"], dd["shared_out"],
+                                                     dd["residual"], dd["gamma"], d["eps"],
+                                                     d["scale"])
+    else:
+        hidden = dd["shared_out"]
+        r0, q0, s0, _ = mfr.residual_add_rmsnorm_fp8(dd["shared_out"], dd["residual"],
+                                                     dd["gamma"], d["eps"])
+    res = dd["residual"].clone()
+    r, q, s = mfr.fused_add_rmsnorm(hidden, res, dd["gamma"], d["eps"], fp8=True,
+                                    in_place=in_place)
+    torch.cuda.synchronize()
+    assert (r is res) == in_place
+    assert q.dtype == torch.float8_e4m3fn and s.shape == (28,)
+    assert torch.equal(r.view(torch.int16), r0.view(torch.int16))
+    assert torch.equal(q.view(torch.uint8), q0.view(torch.uint8))
+    assert torch.equal(s.view(torch.int32), s0.view(torch.int32))
+
+
+def test_fp8_custom_ops_pass_opcheck():
+    d = synth.generate(4, 2048, 8, seed=69)
+    dd = gu.to_device(d)
+    ro = torch.empty_like(dd["residual"])
+    # the codes as uint8 (the ops take either): opcheck's schema check compares
+    # tensor values with arithmetic that torch does not provide for float8
+    q = torch.empty(dd["residual"].shape, dtype=torch.uint8, device="cuda")
+    s = torch.empty((4,), dtype=torch.float32, device="cuda")
+    routed = (dd["expert_out"], dd["perm_idx"], dd["topk_w"], dd["shared_out"])
+    utils = ("test_schema", "test_faketensor")
+    torch.library.opcheck(torch.ops.mfr.moe_finalize_rmsnorm_fp8.default,
+                          routed + (dd["residual"], dd["gamma"], d["eps"], d["scale"], ro, q, s),
+                          test_utils=utils)
+    torch.library.opcheck(torch.ops.mfr.moe_finalize_rmsnorm_fp8_.default,
+                          routed + (dd["residual"].clone(), dd["gamma"], d["eps"], d["scale"], q, s),
+                          test_utils=utils)
+    torch.library.opcheck(torch.ops.mfr.residual_add_rmsnorm_fp8.default,
+                          (dd["shared_out"], dd["residual"], dd["gamma"], d["eps"], ro, q, s),
+                          test_utils=utils)
+    torch.library.opcheck(torch.ops.mfr.residual_add_rmsnorm_fp8_.default,
+                          (dd["shared_out"], dd["residual"].clone(), dd["gamma"], d["eps"], q, s),
+                          test_utils=utils)

@@ -108,3 +108,75 @@ def test_dense_graph_replay():
         torch.cuda.synchronize()
         assert np.array_equal(gu.host_u16(r_out), r_eager), i
         assert np.array_equal(gu.host_u16(n_out), n_eager), i
+
+
+# --- the dense tail with FP8 output --------------------------------------
+
+def run_dense_fp8(d, path=0, vpt=0, store=0, bf16_normed=True):
+    x, res, g = gu.dev_bf16(d["x"]), gu.dev_bf16(d["residual"]), gu.dev_bf16(d["gamma"])
+    with gu.forced(path, vpt, store):
+        r, q, sc, n = mfr.residual_add_rmsnorm_fp8(x, res, g, d["eps"], bf16_normed=bf16_normed)
+    torch.cuda.synchronize()
+    return (gu.host_u16(r), q.view(torch.uint8).cpu().numpy(), sc.cpu().numpy().astype(np.float64),
+            None if n is None else gu.host_u16(n))
+
+
+FP8_CASES = [(1, 6144), (28, 6144), (512, 6144), (3, 8), (7, 1000), (33, 6152), (2, 16384)]
+
+
+@pytest.mark.parametrize("path", [0, mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["auto", "token", "stream"])
+@pytest.mark.parametrize("T,H", FP8_CASES, ids=[f"T{t}-H{h}" for t, h in FP8_CASES])
+def test_dense_fp8_parity(T, H, path):
+    """Codes and scales against the oracle's per-token E4M3 quantisation of
+    its exact normed rows; the bf16 outputs bit-identical to the plain dense
+    call."""
+    from tests.test_fp8_gpu import check_fp8
+    d = synth.dense_inputs(T, H, seed=7000 + T + H)
+    r, q, sc, n = run_dense_fp8(d, path=path)
+    r0, n0 = run_dense(d, path=path)
+    assert np.array_equal(r, r0) and np.array_equal(n, n0)
+    ref = oracle.residual_rmsnorm(d["x"], d["residual"], d["gamma"], d["eps"])
+    check_fp8(q, sc, ref, d["gamma"], d["eps"])
+    # without the bf16 normed output: the same codes and scales
+    r2, q2, sc2, n2 = run_dense_fp8(d, path=path, bf16_normed=False)
+    assert n2 is None and np.array_equal(r2, r) and np.array_equal(q2, q)
+    assert np.array_equal(sc2, sc)
+
+
+def test_dense_fp8_prefill_full_size_sampled():
+    from tests.test_fp8_gpu import check_fp8
+    d = synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192), spike_frac=0.01)
+    r, q, sc, _ = run_dense_fp8(d, bf16_normed=False)
+    rng = np.random.default_rng(4)
+    tokens = np.unique(np.concatenate([d["spike_rows"], rng.choice(8192, 200, replace=False)]))
+    ref = oracle.residual_rmsnorm(d["x"][tokens], d["residual"][tokens], d["gamma"], d["eps"])
+    gu.assert_gate(r[tokens], ref["s"], ref["residual_out"], "residual_out")
+    check_fp8(q[tokens], sc[tokens], ref, d["gamma"], d["eps"])
+
+
+def test_dense_fp8_graph_replay():
+    d = synth.dense_inputs(64, 6144, seed=71)
+    x, res, g = gu.dev_bf16(d["x"]), gu.dev_bf16(d["residual"]), gu.dev_bf16(d["gamma"])
+    r0, q0, s0, _ = mfr.residual_add_rmsnorm_fp8(x, res, g, d["eps"])
+    ro, q, s = torch.empty_like(r0), torch.empty_like(q0), torch.empty_like(s0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mfr.residual_add_rmsnorm_fp8(x, res, g, d["eps"], residual_out=ro, normed_fp8=q,
+                                     fp8_scale=s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mfr.residual_add_rmsnorm_fp8(x, res, g, d["eps"], residual_out=ro, normed_fp8=q,
+                                     fp8_scale=s)
+    for _ in range(5):
+        ro.zero_()
+        q.view(torch.uint8).zero_()
+        s.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ro.view(torch.int16), r0.view(torch.int16))
+        assert torch.equal(q.view(torch.uint8), q0.view(torch.uint8))
+        assert torch.equal(s.view(torch.int32), s0.view(torch.int32))

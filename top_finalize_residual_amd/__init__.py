@@ -4,7 +4,8 @@ The op (vLLM pull request #62174, Details): for each token, the weighted sum
 of its K routed-expert GEMM2 rows gathered through a permutation map, times
 the routed scaling factor, plus the shared-expert output and the residual,
 rounded once to bf16 for the new residual stream, then RMSNorm with gamma and
-eps. Also the same tail with no routed part (residual_add_rmsnorm). Both are
+eps. Also the same tail with no routed part (residual_add_rmsnorm), and both
+with the normalised output as dynamic per-token FP8 (the _fp8 forms). All are
 hand-written HIP kernels for gfx950 behind a C ABI
 (include/moe_finalize_rmsnorm.h); this package is the thin Python binding.
 """
@@ -24,6 +25,8 @@ from .binding import (  # noqa: F401
     moe_finalize_rmsnorm_path,
     moe_finalize_rmsnorm_raw,
     residual_add_rmsnorm,
+    residual_add_rmsnorm_fp8,
+    residual_add_rmsnorm_fp8_raw,
     residual_add_rmsnorm_raw,
     strerror,
 )

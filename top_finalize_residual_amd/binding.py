@@ -49,6 +49,9 @@ _lib.moe_finalize_rmsnorm_fp8.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_float
                                           _p, _p, _p, _p, _i64, _i64, _i64, _p]
 _lib.residual_add_rmsnorm.restype = ctypes.c_int
 _lib.residual_add_rmsnorm.argtypes = [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _p]
+_lib.residual_add_rmsnorm_fp8.restype = ctypes.c_int
+_lib.residual_add_rmsnorm_fp8.argtypes = [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _i64, _i64,
+                                          _p]
 _lib.moe_finalize_rmsnorm_checked.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_checked.argtypes = [_p, _i64, _p, _p, _p, _p, _p, ctypes.c_float,
                                               ctypes.c_float, _p, _p, _p, _i64, _i64, _i64, _p]
@@ -251,6 +254,35 @@ def residual_add_rmsnorm(x, residual, gamma, eps, residual_out=None, normed_out=
     return residual_out, normed_out
 
 
+def _fp8_outputs(T, H, dev, residual_out, normed_fp8, fp8_scale, normed_out, bf16_normed):
+    """Allocates the outputs of an FP8-output call that were not given and
+    checks all of them: residual_out [T, H] bf16, normed_fp8 [T, H] E4M3 (or
+    uint8), fp8_scale [T] fp32, and normed_out [T, H] bf16 when it is written
+    (given, or asked for with bf16_normed)."""
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if normed_fp8 is None:
+        normed_fp8 = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev)
+    if fp8_scale is None:
+        fp8_scale = torch.empty((T,), dtype=torch.float32, device=dev)
+    if normed_out is None and bf16_normed:
+        normed_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(residual_out, "residual_out", torch.bfloat16, 2)
+    if normed_fp8.dtype not in (torch.float8_e4m3fn, torch.uint8) or not normed_fp8.is_cuda or \
+            not normed_fp8.is_contiguous() or tuple(normed_fp8.shape) != (T, H):
+        raise ValueError("normed_fp8 must be a contiguous [T, H] float8_e4m3fn (or uint8) GPU tensor")
+    if tuple(residual_out.shape) != (T, H):
+        raise ValueError("residual_out must be [T, H]")
+    _check(fp8_scale, "fp8_scale", torch.float32, 1)
+    if tuple(fp8_scale.shape) != (T,):
+        raise ValueError(f"fp8_scale has shape {tuple(fp8_scale.shape)}, expected {(T,)}")
+    if normed_out is not None:
+        _check(normed_out, "normed_out", torch.bfloat16, 2)
+        if tuple(normed_out.shape) != (T, H):
+            raise ValueError("normed_out must be [T, H]")
+    return residual_out, normed_fp8, fp8_scale, normed_out
+
+
 def moe_finalize_rmsnorm_fp8_raw(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
                                  scale, residual_out, normed_out, normed_fp8, fp8_scale, T, H, K,
                                  stream):
@@ -281,27 +313,8 @@ def moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual,
             tuple(residual.shape) != (T, H) or tuple(topk_w.shape) != (T, K):
         raise ValueError("inconsistent shapes")
     dev = residual.device
-    if residual_out is None:
-        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    if normed_fp8 is None:
-        normed_fp8 = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev)
-    if fp8_scale is None:
-        fp8_scale = torch.empty((T,), dtype=torch.float32, device=dev)
-    if normed_out is None and bf16_normed:
-        normed_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    _check(residual_out, "residual_out", torch.bfloat16, 2)
-    if normed_fp8.dtype not in (torch.float8_e4m3fn, torch.uint8) or not normed_fp8.is_cuda or \
-            not normed_fp8.is_contiguous() or tuple(normed_fp8.shape) != (T, H):
-        raise ValueError("normed_fp8 must be a contiguous [T, H] float8_e4m3fn (or uint8) GPU tensor")
-    if tuple(residual_out.shape) != (T, H):
-        raise ValueError("residual_out must be [T, H]")
-    _check(fp8_scale, "fp8_scale", torch.float32, 1)
-    if tuple(fp8_scale.shape) != (T,):
-        raise ValueError(f"fp8_scale has shape {tuple(fp8_scale.shape)}, expected {(T,)}")
-    if normed_out is not None:
-        _check(normed_out, "normed_out", torch.bfloat16, 2)
-        if tuple(normed_out.shape) != (T, H):
-            raise ValueError("normed_out must be [T, H]")
+    residual_out, normed_fp8, fp8_scale, normed_out = _fp8_outputs(
+        T, H, dev, residual_out, normed_fp8, fp8_scale, normed_out, bf16_normed)
     _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out,
                  normed_fp8, fp8_scale, normed_out)
     stream, ctx = _launch_context(dev, stream)
@@ -311,6 +324,45 @@ def moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual,
             residual.data_ptr(), gamma.data_ptr(), float(eps), float(scale),
             residual_out.data_ptr(), normed_out.data_ptr() if normed_out is not None else None,
             normed_fp8.data_ptr(), fp8_scale.data_ptr(), T, H, K, stream.cuda_stream)
+    if rc != MFR_OK:
+        raise MFRError(rc)
+    return residual_out, normed_fp8, fp8_scale, normed_out
+
+
+def residual_add_rmsnorm_fp8_raw(x, residual, gamma, eps, residual_out, normed_out, normed_fp8,
+                                 fp8_scale, T, H, stream):
+    """Direct C call with integer addresses (normed_out may be 0/None); returns the status."""
+    return _lib.residual_add_rmsnorm_fp8(x, residual, gamma, float(eps), residual_out,
+                                         normed_out or None, normed_fp8, fp8_scale, int(T), int(H),
+                                         stream)
+
+
+def residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=None, normed_fp8=None,
+                             fp8_scale=None, bf16_normed=False, normed_out=None, stream=None):
+    """Dense residual add + RMSNorm with the normalised output as dynamic
+    per-token FP8 (E4M3).
+
+    x / residual [T, H] bf16, gamma [H] bf16. Returns (residual_out, normed_fp8
+    [T, H] torch.float8_e4m3fn, fp8_scale [T] float32, normed_out or None); the
+    bf16 normed output is written only when bf16_normed is true or normed_out
+    is given. residual_out may be `residual` itself.
+    """
+    _check(x, "x", torch.bfloat16, 2)
+    _check(residual, "residual", torch.bfloat16, 2)
+    _check(gamma, "gamma", torch.bfloat16, 1)
+    T, H = x.shape
+    if tuple(residual.shape) != (T, H) or gamma.shape[0] != H:
+        raise ValueError("inconsistent shapes")
+    dev = residual.device
+    residual_out, normed_fp8, fp8_scale, normed_out = _fp8_outputs(
+        T, H, dev, residual_out, normed_fp8, fp8_scale, normed_out, bf16_normed)
+    _same_device(x, residual, gamma, residual_out, normed_fp8, fp8_scale, normed_out)
+    stream, ctx = _launch_context(dev, stream)
+    with ctx:
+        rc = _lib.residual_add_rmsnorm_fp8(
+            x.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
+            residual_out.data_ptr(), normed_out.data_ptr() if normed_out is not None else None,
+            normed_fp8.data_ptr(), fp8_scale.data_ptr(), T, H, stream.cuda_stream)
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_fp8, fp8_scale, normed_out

@@ -744,6 +744,42 @@ int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint
     return launch(p, T, H, kDense, mfr::kOutBf16, stream);
 }
 
+int residual_add_rmsnorm_fp8(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                             float eps, uint16_t* residual_out, uint16_t* normed_out,
+                             uint8_t* normed_fp8, float* fp8_scale, int64_t T, int64_t H,
+                             hipStream_t stream) {
+    if (!shape_ok(T, H, 1)) return MFR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return MFR_ERR_SCALAR;
+    if (T == 0) return MFR_OK;
+    if (!x || !residual || !gamma || !residual_out || !normed_fp8 || !fp8_scale) return MFR_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gamma, 16) ||
+        !aligned(residual_out, 16) || (normed_out && !aligned(normed_out, 16)) ||
+        !aligned(normed_fp8, 8) || !aligned(fp8_scale, 4))
+        return MFR_ERR_ALIGN;
+    const uint64_t act = static_cast<uint64_t>(T) * H * 2;
+    const Extent outs[] = {{residual_out, act},
+                           {normed_fp8, static_cast<uint64_t>(T) * H},
+                           {fp8_scale, static_cast<uint64_t>(T) * 4},
+                           {normed_out, normed_out ? act : 0}};
+    const Extent ins[] = {{residual, act}, {x, act}, {gamma, static_cast<uint64_t>(H) * 2}};
+    const int rc = check_aliasing(outs, 4, ins, 3, residual_out, residual);
+    if (rc != MFR_OK) return rc;
+
+    mfr::Params p = {};
+    p.shared_out = reinterpret_cast<const mfr::u32x4*>(x);
+    p.residual = reinterpret_cast<const mfr::u32x4*>(residual);
+    p.gamma = reinterpret_cast<const mfr::u32x4*>(gamma);
+    p.residual_out = reinterpret_cast<mfr::u32x4*>(residual_out);
+    p.normed_out = reinterpret_cast<mfr::u32x4*>(normed_out);
+    p.normed_fp8 = normed_fp8;
+    p.fp8_scale = fp8_scale;
+    p.eps = eps;
+    p.scale = 1.0f;
+    p.K = 0;
+    p.rows = kNoRowBound;
+    return launch(p, T, H, kDense, normed_out ? mfr::kOutBoth : mfr::kOutFp8, stream);
+}
+
 int moe_finalize_rmsnorm_path(int64_t T, int64_t H, int64_t K) {
     if (!shape_ok(T, H, K)) return MFR_PATH_UNSUPPORTED;
     return choose_path(T == 0 ? 1 : T);

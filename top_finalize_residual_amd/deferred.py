@@ -21,7 +21,9 @@ Here:
     records them: ``mfr::moe_finalize_rmsnorm`` and ``mfr::residual_add_rmsnorm``
     write a separate residual_out; ``mfr::moe_finalize_rmsnorm_`` and
     ``mfr::residual_add_rmsnorm_`` update the residual stream in place (it is
-    then the one mutated argument, never passed twice).
+    then the one mutated argument, never passed twice); the ``_fp8`` forms of
+    all four write the normed state as per-token FP8 codes and scales, the
+    activation format of an FP8 projection.
 Every step of the arithmetic runs in the HIP library; nothing here computes.
 """
 from dataclasses import dataclass
@@ -70,6 +72,71 @@ def _residual_add_rmsnorm_inplace_op(x: torch.Tensor, residual: torch.Tensor,
                                      normed_out: torch.Tensor) -> None:
     binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual,
                                  normed_out=normed_out)
+
+
+@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm_fp8",
+                         mutates_args=("residual_out", "normed_fp8", "fp8_scale"))
+def _moe_finalize_rmsnorm_fp8_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
+                                 topk_w: torch.Tensor, shared_out: torch.Tensor,
+                                 residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                                 scale: float, residual_out: torch.Tensor, normed_fp8: torch.Tensor,
+                                 fp8_scale: torch.Tensor) -> None:
+    binding.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
+                                     eps, scale, residual_out=residual_out, normed_fp8=normed_fp8,
+                                     fp8_scale=fp8_scale)
+
+
+@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm_fp8_",
+                         mutates_args=("residual", "normed_fp8", "fp8_scale"))
+def _moe_finalize_rmsnorm_fp8_inplace_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
+                                         topk_w: torch.Tensor, shared_out: torch.Tensor,
+                                         residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                                         scale: float, normed_fp8: torch.Tensor,
+                                         fp8_scale: torch.Tensor) -> None:
+    binding.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
+                                     eps, scale, residual_out=residual, normed_fp8=normed_fp8,
+                                     fp8_scale=fp8_scale)
+
+
+@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm_fp8",
+                         mutates_args=("residual_out", "normed_fp8", "fp8_scale"))
+def _residual_add_rmsnorm_fp8_op(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                                 eps: float, residual_out: torch.Tensor, normed_fp8: torch.Tensor,
+                                 fp8_scale: torch.Tensor) -> None:
+    binding.residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=residual_out,
+                                     normed_fp8=normed_fp8, fp8_scale=fp8_scale)
+
+
+@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm_fp8_",
+                         mutates_args=("residual", "normed_fp8", "fp8_scale"))
+def _residual_add_rmsnorm_fp8_inplace_op(x: torch.Tensor, residual: torch.Tensor,
+                                         gamma: torch.Tensor, eps: float,
+                                         normed_fp8: torch.Tensor,
+                                         fp8_scale: torch.Tensor) -> None:
+    binding.residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=residual,
+                                     normed_fp8=normed_fp8, fp8_scale=fp8_scale)
+
+
+@_moe_finalize_rmsnorm_fp8_op.register_fake
+def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
+      normed_fp8, fp8_scale):
+    return None
+
+
+@_moe_finalize_rmsnorm_fp8_inplace_op.register_fake
+def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, normed_fp8,
+      fp8_scale):
+    return None
+
+
+@_residual_add_rmsnorm_fp8_op.register_fake
+def _(x, residual, gamma, eps, residual_out, normed_fp8, fp8_scale):
+    return None
+
+
+@_residual_add_rmsnorm_fp8_inplace_op.register_fake
+def _(x, residual, gamma, eps, normed_fp8, fp8_scale):
+    return None
 
 
 @_moe_finalize_rmsnorm_op.register_fake
@@ -137,24 +204,52 @@ def defer_moe_finalize(num_tokens: int, hidden_size: int, top_k: int) -> bool:
     return binding.moe_finalize_rmsnorm_path(num_tokens, hidden_size, top_k) != binding.PATH_UNSUPPORTED
 
 
-def _outputs(ref: torch.Tensor, residual: torch.Tensor, residual_out, normed_out, in_place):
-    """(residual_out or None for an in-place update, normed_out)."""
+def _residual_out(ref: torch.Tensor, residual: torch.Tensor, residual_out, in_place):
+    """The separate output for the new residual stream, or None for an
+    in-place update of `residual`."""
     if residual_out is residual:
-        in_place = True
-    elif in_place and residual_out is not None:
-        raise ValueError("in_place=True writes the residual stream itself; pass no residual_out")
-    if not in_place and residual_out is None:
-        residual_out = torch.empty_like(ref)
-    if normed_out is None:
-        normed_out = torch.empty_like(ref)
-    return (None if in_place else residual_out), normed_out
+        return None
+    if in_place:
+        if residual_out is not None:
+            raise ValueError("in_place=True writes the residual stream itself; pass no residual_out")
+        return None
+    return torch.empty_like(ref) if residual_out is None else residual_out
+
+
+def _routed(hidden: "MoEOutput"):
+    """(rows, perm_idx, weights, scale) of a MoEOutput's routed part."""
+    if hidden.deferred:
+        r = hidden.routed
+        return r.expert_out, r.perm_idx, r.topk_w, float(r.scale)
+    # An already finalized routed part goes through the same kernel as a single
+    # routed row per token (weight 1, scale 1), which keeps the one-rounding
+    # contract for routed + shared + residual.
+    rows = hidden.routed
+    T = rows.shape[0]
+    idx = torch.arange(T, dtype=torch.int32, device=rows.device).unsqueeze(1)
+    w = torch.ones((T, 1), dtype=torch.float32, device=rows.device)
+    return rows, idx, w, 1.0
+
+
+# (routed part, FP8 output, in place) -> custom op
+_OPS = {
+    (True, False, False): "moe_finalize_rmsnorm",
+    (True, False, True): "moe_finalize_rmsnorm_",
+    (True, True, False): "moe_finalize_rmsnorm_fp8",
+    (True, True, True): "moe_finalize_rmsnorm_fp8_",
+    (False, False, False): "residual_add_rmsnorm",
+    (False, False, True): "residual_add_rmsnorm_",
+    (False, True, False): "residual_add_rmsnorm_fp8",
+    (False, True, True): "residual_add_rmsnorm_fp8_",
+}
 
 
 def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Tensor,
                       gamma: torch.Tensor, eps: float, *, in_place: bool = False,
                       residual_out: Optional[torch.Tensor] = None,
-                      normed_out: Optional[torch.Tensor] = None
-                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+                      normed_out: Optional[torch.Tensor] = None, fp8: bool = False,
+                      normed_fp8: Optional[torch.Tensor] = None,
+                      fp8_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, ...]:
     """The consumer norm of the next layer.
 
     hidden: a MoEOutput (deferred or finalized routed part plus shared output)
@@ -162,33 +257,35 @@ def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Te
     Returns (new residual stream, normed hidden state), both [T, H] bf16.
     in_place: write the new residual stream into `residual` itself (also
     implied by passing residual_out=residual).
+    fp8: produce the normed hidden state as dynamic per-token FP8 for an FP8
+    projection instead: returns (new residual stream, normed_fp8 [T, H]
+    float8_e4m3fn, fp8_scale [T] float32), where a token's normed row is
+    about normed_fp8 times its scale. normed_fp8 and fp8_scale may be given.
     """
-    if isinstance(hidden, MoEOutput):
-        shared = hidden.shared
-        residual_out, normed_out = _outputs(shared, residual, residual_out, normed_out, in_place)
-        if hidden.deferred:
-            r = hidden.routed
-            rows, idx, w, scale = r.expert_out, r.perm_idx, r.topk_w, float(r.scale)
-        else:
-            # An already finalized routed part goes through the same kernel as
-            # a single routed row per token (weight 1, scale 1), which keeps
-            # the one-rounding contract for routed + shared + residual.
-            rows = hidden.routed
-            T = rows.shape[0]
-            idx = torch.arange(T, dtype=torch.int32, device=rows.device).unsqueeze(1)
-            w = torch.ones((T, 1), dtype=torch.float32, device=rows.device)
-            scale = 1.0
-        if residual_out is None:
-            torch.ops.mfr.moe_finalize_rmsnorm_(rows, idx, w, shared, residual, gamma, float(eps),
-                                                scale, normed_out)
-            return residual, normed_out
-        torch.ops.mfr.moe_finalize_rmsnorm(rows, idx, w, shared, residual, gamma, float(eps), scale,
-                                           residual_out, normed_out)
-        return residual_out, normed_out
-    residual_out, normed_out = _outputs(hidden, residual, residual_out, normed_out, in_place)
-    if residual_out is None:
-        torch.ops.mfr.residual_add_rmsnorm_(hidden, residual, gamma, float(eps), normed_out)
-        return residual, normed_out
-    torch.ops.mfr.residual_add_rmsnorm(hidden, residual, gamma, float(eps), residual_out,
-                                       normed_out)
-    return residual_out, normed_out
+    if fp8 and normed_out is not None:
+        raise ValueError("fp8=True writes normed_fp8 and fp8_scale, not normed_out")
+    if not fp8 and (normed_fp8 is not None or fp8_scale is not None):
+        raise ValueError("normed_fp8 and fp8_scale are the outputs of fp8=True")
+    moe = isinstance(hidden, MoEOutput)
+    ref = hidden.shared if moe else hidden
+    r_out = _residual_out(ref, residual, residual_out, in_place)
+    if fp8:
+        T, H = ref.shape
+        if normed_fp8 is None:
+            normed_fp8 = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=ref.device)
+        if fp8_scale is None:
+            fp8_scale = torch.empty((T,), dtype=torch.float32, device=ref.device)
+        outs = (normed_fp8, fp8_scale)
+    else:
+        outs = (torch.empty_like(ref) if normed_out is None else normed_out,)
+    if moe:
+        rows, idx, w, scale = _routed(hidden)
+        args = (rows, idx, w, hidden.shared, residual, gamma, float(eps), scale)
+    else:
+        args = (hidden, residual, gamma, float(eps))
+    op = getattr(torch.ops.mfr, _OPS[(moe, fp8, r_out is None)])
+    if r_out is None:
+        op(*args, *outs)
+        return (residual,) + outs
+    op(*args, r_out, *outs)
+    return (r_out,) + outs
