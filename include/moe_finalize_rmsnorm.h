@@ -160,6 +160,23 @@ int moe_finalize_rmsnorm_fp8(const uint16_t* expert_out, const int32_t* perm_idx
                              uint8_t* normed_fp8, float* fp8_scale,
                              int64_t T, int64_t H, int64_t K, hipStream_t stream);
 
+/* The FP8-output op told the row count R of expert_out: the row bound and
+ * the flag of moe_finalize_rmsnorm_checked, the outputs of
+ * moe_finalize_rmsnorm_fp8. An index at or past R is treated as masked and
+ * sets *bad_index to 1 when bad_index is not NULL (the flag is never cleared
+ * by the library). For in-range indices every output is bit-identical to
+ * that of moe_finalize_rmsnorm_fp8 with the same arguments; with the flag
+ * raised they are those of moe_finalize_rmsnorm_fp8 with the offending slots
+ * masked. Limits, alignment, aliasing and errors as for the two calls it
+ * combines; the overlap check covers all R rows of expert_out. */
+int moe_finalize_rmsnorm_fp8_checked(const uint16_t* expert_out, int64_t R,
+                                     const int32_t* perm_idx, const float* topk_w,
+                                     const uint16_t* shared_out, const uint16_t* residual,
+                                     const uint16_t* gamma, float eps, float scale,
+                                     uint16_t* residual_out, uint16_t* normed_out,
+                                     uint8_t* normed_fp8, float* fp8_scale, int32_t* bad_index,
+                                     int64_t T, int64_t H, int64_t K, hipStream_t stream);
+
 /* Dense residual add + RMSNorm: the same tail with no routed part, for the
  * layers whose row-parallel attention / MLP outputs, or the final main-model
  * and MTP norms, feed the residual stream ("Port the validated GLM-5.2 H200

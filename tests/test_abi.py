@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
                  "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force",
                  "residual_add_rmsnorm", "moe_finalize_rmsnorm_fp8",
-                 "moe_finalize_rmsnorm_checked", "residual_add_rmsnorm_fp8"):
+                 "moe_finalize_rmsnorm_checked", "residual_add_rmsnorm_fp8",
+                 "moe_finalize_rmsnorm_fp8_checked"):
         assert want in names
 
 
@@ -312,3 +313,34 @@ def test_checked_validation():
     assert binding.lib().moe_finalize_rmsnorm_checked(None, 0, None, None, None, None, None, 1e-6,
                                                       1.0, None, None, None, 0, H, K,
                                                       None) == binding.MFR_OK
+
+
+def fp8_checked_call(T_=T, H_=H, K_=K, R=T * K, eps=1e-6, **over):
+    act = T * H * 2
+    p = dict(_ptrs(), normed_fp8=A + 80 * act, fp8_scale=A + 90 * act, bad_index=A + 91 * act)
+    p.update(over)
+    return mfr.moe_finalize_rmsnorm_fp8_checked_raw(
+        p["expert_out"], R, p["perm_idx"], p["topk_w"], p["shared_out"], p["residual"], p["gamma"],
+        eps, 2.5, p["residual_out"], p["normed_out"], p["normed_fp8"], p["fp8_scale"],
+        p["bad_index"], T_, H_, K_, None)
+
+
+def test_fp8_checked_validation():
+    """moe_finalize_rmsnorm_fp8_checked: the FP8 call's checks plus R and the
+    flag, with the overlap check over all R rows of expert_out."""
+    act = T * H * 2
+    p = dict(_ptrs(), normed_fp8=A + 80 * act, fp8_scale=A + 90 * act, bad_index=A + 91 * act)
+    assert fp8_checked_call(R=-1) == binding.MFR_ERR_SHAPE
+    assert fp8_checked_call(H_=12) == binding.MFR_ERR_SHAPE
+    assert fp8_checked_call(eps=-1.0) == binding.MFR_ERR_SCALAR
+    for name in ("perm_idx", "topk_w", "shared_out", "residual", "gamma", "residual_out",
+                 "normed_fp8", "fp8_scale", "expert_out"):
+        assert fp8_checked_call(**{name: None}) == binding.MFR_ERR_NULL, name
+    assert fp8_checked_call(normed_fp8=p["normed_fp8"] + 4) == binding.MFR_ERR_ALIGN
+    assert fp8_checked_call(bad_index=p["bad_index"] + 2) == binding.MFR_ERR_ALIGN
+    assert fp8_checked_call(bad_index=p["fp8_scale"]) == binding.MFR_ERR_ALIAS
+    assert fp8_checked_call(normed_fp8=p["expert_out"] + (T * K // 2) * H * 2) == \
+        binding.MFR_ERR_ALIAS  # inside the R rows
+    # the optional outputs are not examined when absent
+    assert fp8_checked_call(normed_out=None, bad_index=None, T_=0) == binding.MFR_OK
+    assert fp8_checked_call(R=0, expert_out=None, T_=0) == binding.MFR_OK

@@ -1,7 +1,7 @@
-"""GPU checks of moe_finalize_rmsnorm_checked, the fused op told the row count
-R of expert_out: in-range indices give the plain op's outputs bit for bit and
-leave the flag clear; an index at or past R is treated as masked and raises
-the flag."""
+"""GPU checks of moe_finalize_rmsnorm_checked and moe_finalize_rmsnorm_fp8_checked,
+the fused op (bf16 or FP8 output) told the row count R of expert_out: in-range
+indices give the plain op's outputs bit for bit and leave the flag clear; an
+index at or past R is treated as masked and raises the flag."""
 import numpy as np
 import pytest
 import torch
@@ -83,4 +83,72 @@ def test_far_index_is_masked_not_read():
                                                   *_args(dd)[2:], d["eps"], d["scale"])
     torch.cuda.synchronize()
     assert np.array_equal(gu.host_u16(r), r0) and np.array_equal(gu.host_u16(n), n0)
+    assert int(flag.item()) == 1
+
+
+# --- the FP8-output form ---------------------------------------------------
+
+def _fp8_plain(dd, d, perm_idx=None):
+    r, q, s, n = mfr.moe_finalize_rmsnorm_fp8(dd["expert_out"],
+                                              dd["perm_idx"] if perm_idx is None else perm_idx,
+                                              *_args(dd)[2:], d["eps"], d["scale"],
+                                              bf16_normed=True)
+    torch.cuda.synchronize()
+    return r, q, s, n
+
+
+def _same(a, b):
+    return all(torch.equal(x.view(torch.uint8), y.view(torch.uint8)) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
+@pytest.mark.parametrize("cfg,T", [("decode", 28), ("decode_masked", 64), ("batch512", 512)])
+def test_fp8_in_range_equals_plain_fp8_call(cfg, T, path):
+    d = synth.config_inputs(cfg, T)
+    dd = gu.to_device(d)
+    with gu.forced(path, 0, 0):
+        want = _fp8_plain(dd, d)
+        r, q, s, n, bad = mfr.moe_finalize_rmsnorm_fp8_checked(*_args(dd), d["eps"], d["scale"],
+                                                               bf16_normed=True)
+    torch.cuda.synchronize()
+    assert _same((r, q, s, n), want)
+    assert int(bad.item()) == 0
+
+
+@pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
+def test_fp8_rows_past_r_are_masked_and_reported(path):
+    """As for the bf16 form: the rows in [R, T*K) are real memory, and the
+    checked FP8 call equals the plain FP8 call with those slots set to -1."""
+    T, H, K = 64, 2048, 12
+    d = synth.generate(T, H, K, scale=2.5, mask_frac=0.05, seed=830, extra_rows=16)
+    R = T * K - 40
+    dd = gu.to_device(d)
+    past = d["perm_idx"] >= R
+    assert past.any()
+    masked = d["perm_idx"].copy()
+    masked[past] = -1
+    with gu.forced(path, 0, 0):
+        want = _fp8_plain(dd, d, torch.from_numpy(masked).cuda())
+        r, q, s, n, bad = mfr.moe_finalize_rmsnorm_fp8_checked(dd["expert_out"][:R],
+                                                               *_args(dd)[1:], d["eps"],
+                                                               d["scale"], bf16_normed=True)
+    torch.cuda.synchronize()
+    assert _same((r, q, s, n), want)
+    assert int(bad.item()) == 1
+
+
+def test_fp8_far_index_is_masked_not_read():
+    T, H, K = 16, 2048, 8
+    d = synth.generate(T, H, K, scale=2.5, seed=840)
+    dd = gu.to_device(d)
+    bad_idx = d["perm_idx"].copy()
+    bad_idx[5, 1] = 2 ** 31 - 1
+    masked = bad_idx.copy()
+    masked[5, 1] = -1
+    want = _fp8_plain(dd, d, torch.from_numpy(masked).cuda())
+    r, q, s, n, flag = mfr.moe_finalize_rmsnorm_fp8_checked(
+        dd["expert_out"], torch.from_numpy(bad_idx).cuda(), *_args(dd)[2:], d["eps"], d["scale"],
+        bf16_normed=True)
+    torch.cuda.synchronize()
+    assert _same((r, q, s, n), want)
     assert int(flag.item()) == 1

@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     moe_finalize_rmsnorm_checked,
     moe_finalize_rmsnorm_force,
     moe_finalize_rmsnorm_fp8,
+    moe_finalize_rmsnorm_fp8_checked,
+    moe_finalize_rmsnorm_fp8_checked_raw,
     moe_finalize_rmsnorm_fp8_raw,
     moe_finalize_rmsnorm_path,
     moe_finalize_rmsnorm_raw,

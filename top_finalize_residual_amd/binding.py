@@ -55,6 +55,10 @@ _lib.residual_add_rmsnorm_fp8.argtypes = [_p, _p, _p, ctypes.c_float, _p, _p, _p
 _lib.moe_finalize_rmsnorm_checked.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_checked.argtypes = [_p, _i64, _p, _p, _p, _p, _p, ctypes.c_float,
                                               ctypes.c_float, _p, _p, _p, _i64, _i64, _i64, _p]
+_lib.moe_finalize_rmsnorm_fp8_checked.restype = ctypes.c_int
+_lib.moe_finalize_rmsnorm_fp8_checked.argtypes = [_p, _i64, _p, _p, _p, _p, _p, ctypes.c_float,
+                                                  ctypes.c_float, _p, _p, _p, _p, _p, _i64, _i64,
+                                                  _i64, _p]
 _lib.moe_finalize_rmsnorm_force.restype = ctypes.c_int
 _lib.moe_finalize_rmsnorm_force.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
 
@@ -215,6 +219,61 @@ def moe_finalize_rmsnorm_checked(expert_out, perm_idx, topk_w, shared_out, resid
     if rc != MFR_OK:
         raise MFRError(rc)
     return residual_out, normed_out, bad_index
+
+
+def moe_finalize_rmsnorm_fp8_checked_raw(expert_out, R, perm_idx, topk_w, shared_out, residual,
+                                         gamma, eps, scale, residual_out, normed_out, normed_fp8,
+                                         fp8_scale, bad_index, T, H, K, stream):
+    """Direct C call with integer addresses (normed_out and bad_index may be
+    0/None); returns the status."""
+    return _lib.moe_finalize_rmsnorm_fp8_checked(
+        expert_out, int(R), perm_idx, topk_w, shared_out, residual, gamma, float(eps),
+        float(scale), residual_out, normed_out or None, normed_fp8, fp8_scale, bad_index or None,
+        int(T), int(H), int(K), stream)
+
+
+def moe_finalize_rmsnorm_fp8_checked(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
+                                     eps, scale, residual_out=None, normed_fp8=None,
+                                     fp8_scale=None, bf16_normed=False, normed_out=None,
+                                     bad_index=None, stream=None):
+    """moe_finalize_rmsnorm_fp8 told R = expert_out.shape[0]: a slot whose
+    index is at or past R is treated as masked, and bad_index (a one-element
+    int32 GPU tensor, allocated zeroed when not given) is set to 1 if any
+    token holds such an index. Returns (residual_out, normed_fp8, fp8_scale,
+    normed_out or None, bad_index)."""
+    _check(expert_out, "expert_out", torch.bfloat16, 2)
+    _check(perm_idx, "perm_idx", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(shared_out, "shared_out", torch.bfloat16, 2)
+    _check(residual, "residual", torch.bfloat16, 2)
+    _check(gamma, "gamma", torch.bfloat16, 1)
+    T, K = perm_idx.shape
+    H = gamma.shape[0]
+    R = expert_out.shape[0]
+    if expert_out.shape[1] != H or tuple(shared_out.shape) != (T, H) or \
+            tuple(residual.shape) != (T, H) or tuple(topk_w.shape) != (T, K):
+        raise ValueError("inconsistent shapes")
+    dev = residual.device
+    residual_out, normed_fp8, fp8_scale, normed_out = _fp8_outputs(
+        T, H, dev, residual_out, normed_fp8, fp8_scale, normed_out, bf16_normed)
+    if bad_index is None:
+        bad_index = torch.zeros((1,), dtype=torch.int32, device=dev)
+    _check(bad_index, "bad_index", torch.int32, 1)
+    if bad_index.numel() < 1:
+        raise ValueError("bad_index must hold one int32")
+    _same_device(expert_out, perm_idx, topk_w, shared_out, residual, gamma, residual_out,
+                 normed_fp8, fp8_scale, normed_out, bad_index)
+    stream, ctx = _launch_context(dev, stream)
+    with ctx:
+        rc = _lib.moe_finalize_rmsnorm_fp8_checked(
+            expert_out.data_ptr(), R, perm_idx.data_ptr(), topk_w.data_ptr(),
+            shared_out.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
+            float(scale), residual_out.data_ptr(),
+            normed_out.data_ptr() if normed_out is not None else None, normed_fp8.data_ptr(),
+            fp8_scale.data_ptr(), bad_index.data_ptr(), T, H, K, stream.cuda_stream)
+    if rc != MFR_OK:
+        raise MFRError(rc)
+    return residual_out, normed_fp8, fp8_scale, normed_out, bad_index
 
 
 def residual_add_rmsnorm_raw(x, residual, gamma, eps, residual_out, normed_out, T, H, stream):

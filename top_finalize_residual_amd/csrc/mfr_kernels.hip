@@ -464,9 +464,8 @@ const void* pick_variant(Variant v, bool wt) {
     switch (v) {
         case kTop8: return pick_store<VPT, 8, QM>(wt);
         case kAnyK: return pick_store<VPT, 0, QM>(wt);
-        // the checked forms exist for the bf16 output only
-        case kTop8Rows: return pick_store<VPT, 8, mfr::kOutBf16, true>(wt);
-        case kAnyKRows: return pick_store<VPT, 0, mfr::kOutBf16, true>(wt);
+        case kTop8Rows: return pick_store<VPT, 8, QM, true>(wt);
+        case kAnyKRows: return pick_store<VPT, 0, QM, true>(wt);
         default: return pick_store<VPT, -1, QM>(wt);
     }
 }
@@ -713,6 +712,59 @@ int moe_finalize_rmsnorm_fp8(const uint16_t* expert_out, const int32_t* perm_idx
     p.rows = kNoRowBound;
     return launch(p, T, H, K == 8 ? kTop8 : kAnyK, normed_out ? mfr::kOutBoth : mfr::kOutFp8,
                   stream);
+}
+
+int moe_finalize_rmsnorm_fp8_checked(const uint16_t* expert_out, int64_t R,
+                                     const int32_t* perm_idx, const float* topk_w,
+                                     const uint16_t* shared_out, const uint16_t* residual,
+                                     const uint16_t* gamma, float eps, float scale,
+                                     uint16_t* residual_out, uint16_t* normed_out,
+                                     uint8_t* normed_fp8, float* fp8_scale, int32_t* bad_index,
+                                     int64_t T, int64_t H, int64_t K, hipStream_t stream) {
+    if (!shape_ok(T, H, K) || R < 0) return MFR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(scale)) return MFR_ERR_SCALAR;
+    if (T == 0) return MFR_OK;
+    if (R > (int64_t{1} << 31)) R = int64_t{1} << 31;
+    if (!perm_idx || !topk_w || !shared_out || !residual || !gamma || !residual_out ||
+        !normed_fp8 || !fp8_scale || (R > 0 && !expert_out))
+        return MFR_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(shared_out, 16) || !aligned(residual, 16) ||
+        !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+        (normed_out && !aligned(normed_out, 16)) || !aligned(normed_fp8, 8) ||
+        !aligned(fp8_scale, 4) || !aligned(perm_idx, 4) || !aligned(topk_w, 4) ||
+        (bad_index && !aligned(bad_index, 4)))
+        return MFR_ERR_ALIGN;
+    const uint64_t act = static_cast<uint64_t>(T) * H * 2;
+    const uint64_t meta = static_cast<uint64_t>(T) * K * 4;
+    const Extent outs[] = {{residual_out, act},
+                           {normed_fp8, static_cast<uint64_t>(T) * H},
+                           {fp8_scale, static_cast<uint64_t>(T) * 4},
+                           {normed_out, normed_out ? act : 0},
+                           {bad_index, bad_index ? 4u : 0u}};
+    const Extent ins[] = {{residual, act}, {shared_out, act}, {gamma, static_cast<uint64_t>(H) * 2},
+                          {perm_idx, meta}, {topk_w, meta},
+                          {expert_out, static_cast<uint64_t>(R) * static_cast<uint64_t>(H) * 2}};
+    const int rc = check_aliasing(outs, 5, ins, 6, residual_out, residual);
+    if (rc != MFR_OK) return rc;
+
+    mfr::Params p = {};
+    p.expert_out = reinterpret_cast<const mfr::u32x4*>(expert_out);
+    p.perm_idx = perm_idx;
+    p.topk_w = topk_w;
+    p.shared_out = reinterpret_cast<const mfr::u32x4*>(shared_out);
+    p.residual = reinterpret_cast<const mfr::u32x4*>(residual);
+    p.gamma = reinterpret_cast<const mfr::u32x4*>(gamma);
+    p.residual_out = reinterpret_cast<mfr::u32x4*>(residual_out);
+    p.normed_out = reinterpret_cast<mfr::u32x4*>(normed_out);
+    p.normed_fp8 = normed_fp8;
+    p.fp8_scale = fp8_scale;
+    p.eps = eps;
+    p.scale = scale;
+    p.K = static_cast<int>(K);
+    p.rows = static_cast<uint32_t>(R);
+    p.bad_index = bad_index;
+    return launch(p, T, H, K == 8 ? kTop8Rows : kAnyKRows,
+                  normed_out ? mfr::kOutBoth : mfr::kOutFp8, stream);
 }
 
 int residual_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
