@@ -119,6 +119,20 @@ int main() {
            "dense outputs alias");
     expect(residual_add_rmsnorm(S, R, G, 1e-6f, RO, NO, 0, H, nullptr), MFR_OK, "dense T = 0");
 
+    // FP8 output with the row bound
+    expect(moe_finalize_rmsnorm_fp8_checked(E, -1, P, W, S, R, G, 1e-6f, 1.f, RO, nullptr, Q, SC,
+                                            FLAG, T, H, K, nullptr),
+           MFR_ERR_SHAPE, "fp8 checked negative R");
+    expect(moe_finalize_rmsnorm_fp8_checked(E, T * K, P, W, S, R, G, 1e-6f, 1.f, RO, nullptr, Q,
+                                            reinterpret_cast<float*>(FLAG), FLAG, T, H, K, nullptr),
+           MFR_ERR_ALIAS, "fp8 checked flag on the scales");
+    expect(moe_finalize_rmsnorm_fp8_checked(E, T * K, P, W, S, R, G, 1e-6f, 1.f, RO, nullptr,
+                                            nullptr, SC, FLAG, T, H, K, nullptr),
+           MFR_ERR_NULL, "fp8 checked null codes");
+    expect(moe_finalize_rmsnorm_fp8_checked(E, T * K, P, W, S, R, G, 1e-6f, 1.f, RO, nullptr, Q, SC,
+                                            FLAG, 0, H, K, nullptr),
+           MFR_OK, "fp8 checked T = 0");
+
     // dense tail with FP8 output
     expect(residual_add_rmsnorm_fp8(S, R, G, 1e-6f, RO, nullptr, nullptr, SC, T, H, nullptr),
            MFR_ERR_NULL, "dense fp8 null codes");
