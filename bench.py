@@ -724,7 +724,7 @@ def summarize_trace(args):
              "| kernel | grid (threads) | workgroup | tokens | calls | avg µs | median µs | p10 µs | p90 µs | min µs | max µs |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
-        short = name.replace("(mfr::Params)", "")
+        short = name.split("(")[0]  # without the argument list
         q = sorted(v)
         p10, p90 = q[int(0.1 * (len(q) - 1))], q[int(0.9 * (len(q) - 1))]
         lines.append(f"| `{short}` | {grid} | {wg} | {grid // wg} | {len(v)} | {statistics.mean(v):.2f} | "

@@ -5,6 +5,9 @@ this file, where the Python binding loads it. Flags:
   --offload-arch=gfx950          CDNA4 (MI355X) code only
   -ffp-contract=off              every FMA in the kernels is written out
   -target-feature -packed-fp32-ops  no packed fp32 VALU ops are emitted
+  -amdgpu-kernarg-preload-count=16   (the fused-op library only) the kernel's
+                                 leading arguments arrive in SGPRs at wave
+                                 launch instead of through a scalar load
 """
 import os
 import subprocess
@@ -22,10 +25,13 @@ HIPFLAGS = [
     "-ffp-contract=off", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Up to 16 SGPRs of leading kernel arguments (the fused kernel passes 14:
+# six pointers and two ints) are loaded by the dispatcher at wave launch.
+PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
-def _hipcc(sources, out, verbose=False):
-    cmd = [HIPCC, *HIPFLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out + ".tmp", *sources]
+def _hipcc(sources, out, verbose=False, extra=()):
+    cmd = [HIPCC, *HIPFLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-o", out + ".tmp", *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,7 +48,7 @@ def _hipcc(sources, out, verbose=False):
 
 def build(verbose=False):
     """Compile the product library and the bench's copy-probe library."""
-    _hipcc([os.path.join(CSRC, "mfr_kernels.hip")], LIB, verbose)
+    _hipcc([os.path.join(CSRC, "mfr_kernels.hip")], LIB, verbose, extra=PRELOAD)
     _hipcc([os.path.join(CSRC, "copy_probe.hip")], PROBE_LIB, verbose)
     return LIB
 

@@ -342,10 +342,27 @@ struct Bound {
 // One workgroup per token. OUT_AUX is the cache policy of the output stores
 // (write-back, or write-through for outputs larger than the L2); QM the
 // OutMode of the normalised output.
+//
+// The pointers and sizes the first loads need come as separate leading
+// arguments, ahead of the Params block: built with kernel-argument preload,
+// the dispatcher places them in SGPRs when the wave launches, so the routing
+// metadata load starts at once instead of behind a scalar load of the
+// argument block. The values are the same as in p; p's copies are replaced.
 template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS = false>
-__global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(Params p) {
+__global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(
+        const int32_t* perm_idx, const float* topk_w, const u32x4* shared_out,
+        const u32x4* residual, const u32x4* gamma, const u32x4* expert_out, int V, int K,
+        Params p) {
     // Per-wave row sums and (FP8 modes) row maxima; 16-byte aligned for vector reads.
     __shared__ __align__(16) float red[2 * MAX_WAVES];
+    p.perm_idx = perm_idx;
+    p.topk_w = topk_w;
+    p.shared_out = shared_out;
+    p.residual = residual;
+    p.gamma = gamma;
+    p.expert_out = expert_out;
+    p.V = V;
+    p.K = K;
     finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(p, static_cast<int64_t>(blockIdx.x), red);
 }
 
@@ -567,7 +584,8 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
         const int64_t n = T - t0 < per ? T - t0 : per;
         mfr::Params q = t0 == 0 ? p : from_token(p, t0);
         q.T = n;
-        void* args[] = {&q};
+        void* args[] = {&q.perm_idx, &q.topk_w, &q.shared_out, &q.residual, &q.gamma,
+                        &q.expert_out, &q.V, &q.K, &q};
         const hipError_t e =
             hipLaunchKernel(kern, dim3(static_cast<uint32_t>(n)), dim3(nt), args, 0, stream);
         if (e != hipSuccess) return MFR_ERR_HIP;
