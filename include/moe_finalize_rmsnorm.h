@@ -18,9 +18,19 @@
  * RMSNorm in one launch (Details); on one GPU the all-reduce is the identity.
  * The page also says the kernel sums in FP32, and that its outputs moved
  * because the per-step roundings of the unfused chain are gone (Claims,
- * Validation): here
- * the sum s is kept in fp32 registers, rounded to bf16 only at the two outputs,
- * and the norm is taken of the unrounded fp32 s.
+ * Validation): here the sum s is kept in fp32 registers, rounded to bf16 only
+ * at the two outputs, and the norm is taken of the unrounded fp32 s.
+ *
+ * Entry points:
+ *   moe_finalize_rmsnorm              the fused op
+ *   moe_finalize_rmsnorm_checked      the fused op, told the row count R
+ *   moe_finalize_rmsnorm_fp8          the fused op, normed output as per-token FP8
+ *   moe_finalize_rmsnorm_fp8_checked  the two above together
+ *   residual_add_rmsnorm              the same tail with no routed part
+ *   residual_add_rmsnorm_fp8          the dense tail with FP8 output
+ *   moe_finalize_rmsnorm_path         host-only: the launch path of a shape
+ *   moe_finalize_rmsnorm_strerror     text of a status code
+ *   moe_finalize_rmsnorm_force        process-wide launch override (testing)
  *
  * Data types and layout (all row-major, contiguous, device memory):
  *   bf16 tensors are passed as raw 16-bit patterns (uint16_t).
