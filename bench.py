@@ -11,8 +11,10 @@ timed region; HIP events on the launch stream bracket exactly --steps calls.
 Printed (stdout, one JSON line): effective HBM GB/s = algorithmic bytes per
 call / time per call, the roofline object for the fused kernel, the oracle's
 CPU baseline on the same workload, and, as context, decode-latency figures for
-T = 1..64 and the 512-token batch, a measured copy ceiling, and the headline
-workload with its gathered rows grouped by expert instead of randomly placed.
+T = 1..64 and the 512-token batch, a measured copy ceiling, the dense tail and
+the FP8-output calls at T = 8192, the host cost of the torch deferred path, and
+the headline workload with its gathered rows grouped by expert instead of
+randomly placed.
 
 Modes used with rocprofv3 (see profiles/):
   --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
