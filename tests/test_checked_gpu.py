@@ -152,3 +152,32 @@ def test_fp8_far_index_is_masked_not_read():
     torch.cuda.synchronize()
     assert _same((r, q, s, n), want)
     assert int(flag.item()) == 1
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_zero_rows(fp8):
+    """R = 0 (an empty expert_out): every slot is past the rows, so each is
+    masked and flagged; the outputs equal the plain call with every slot
+    masked. With every index already negative, the flag stays clear."""
+    T, H, K = 12, 2048, 8
+    d = synth.generate(T, H, K, scale=2.5, seed=850)
+    dd = gu.to_device(d)
+    empty = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    all_masked = torch.full((T, K), -1, dtype=torch.int32, device="cuda")
+    for idx, flag in ((dd["perm_idx"], 1), (all_masked, 0)):
+        if fp8:
+            want = _fp8_plain(dd, d, all_masked)
+            r, q, s, n, bad = mfr.moe_finalize_rmsnorm_fp8_checked(
+                empty, idx, *_args(dd)[2:], d["eps"], d["scale"], bf16_normed=True)
+            got = (r, q, s, n)
+        else:
+            want = gu.run(dict(dd, perm_idx=all_masked), d["eps"], d["scale"])
+            r, n, bad = mfr.moe_finalize_rmsnorm_checked(empty, idx, *_args(dd)[2:], d["eps"],
+                                                         d["scale"])
+            got = (r, n)
+        torch.cuda.synchronize()
+        if fp8:
+            assert _same(got, want)
+        else:
+            assert np.array_equal(gu.host_u16(r), want[0]) and np.array_equal(gu.host_u16(n), want[1])
+        assert int(bad.item()) == flag
