@@ -375,10 +375,15 @@ def decode_latency(cold_bytes=600_000_000):
         copies, together above cold_bytes, more than twice the Infinity
         Cache), as a decode step reading rows nothing has touched since they
         were written.
+      * producer_written: each call's rows and shared output were written by
+        a producer kernel just before it (copies standing in for GEMM2 and
+        the shared expert), the state a decode step meets inside a layer;
+        the figure is the fused call's share of a graph of producer + call
+        pairs, minus a graph of the producers alone.
     Also the FP8-output and dense variants at T = 28, and the empty-kernel
     floor. Context figures, not the headline."""
     import synth
-    same, fresh = {}, {}
+    same, fresh, produced = {}, {}, {}
     variants = {}
     for T in DECODE_TS:
         d = synth.config_inputs("decode", T)
@@ -397,11 +402,66 @@ def decode_latency(cold_bytes=600_000_000):
                 same[f"T{T}"], fresh[f"T{T}"] = a, b
             else:
                 variants[f"{mode}_T{T}"] = {"same_inputs": a, "fresh_inputs": b}
+        produced[f"T{T}"] = producer_written_us(d)
     # the floor under each decode launch: an empty kernel of the token
     # path's launch shape (T workgroups of 768 threads at H = 6144)
     floor = {f"T{T}": launch_floor_us(T, 768) for T in DECODE_TS}
-    return {"same_inputs": same, "fresh_inputs": fresh, **variants,
+    return {"same_inputs": same, "fresh_inputs": fresh, "producer_written": produced, **variants,
             "empty_kernel_floor": floor}
+
+
+def _graph_us(fn, calls_per_graph, replays=5):
+    """Mean µs per call of a captured graph of fn(), which enqueues
+    calls_per_graph calls (after one eager warm-up on a side stream)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(replays):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
+
+
+def producer_written_us(d, n=64):
+    """The fused call's µs when a producer has just written its rows and
+    shared output: n buffer sets, each rewritten by two device copies (the
+    stand-ins for GEMM2 and the shared expert) right before its call. The
+    result is the per-pair time minus the per-iteration time of the copies
+    alone, both graph-replayed after a cache scrub."""
+    calls = stacked_calls(d, n, "bf16")
+    st = calls[0].keep[0]  # the stacked device inputs, [n, ...] per tensor
+    rows, shared = st["expert_out"][0].clone(), st["shared_out"][0].clone()
+
+    def produce(i):
+        st["expert_out"][i].copy_(rows)
+        st["shared_out"][i].copy_(shared)
+
+    def pairs():
+        for i in range(n):
+            produce(i)
+            calls[i]()
+
+    def producers():
+        for i in range(n):
+            produce(i)
+    scrub_infinity_cache()
+    t_pair = _graph_us(pairs, n)
+    scrub_infinity_cache()
+    t_prod = _graph_us(producers, n)
+    return round(t_pair - t_prod, 2)
 
 
 def graph_ceiling_batch():
