@@ -257,6 +257,21 @@ def cpu_baseline(d, min_seconds=10.0, max_passes=20):
                                     want_exact=False)
             passes += 1
         dt = time.perf_counter() - t0
+        # the smaller workloads beside their GPU figures: median of 3 runs each
+        small = {}
+        for cfg, T in (("decode", 28), ("batch512", 512)):
+            ds = synth.config_inputs(cfg, T)
+            runs = []
+            for _ in range(3):
+                t1 = time.perf_counter()
+                oracle.finalize_rmsnorm(ds["expert_out"], ds["perm_idx"], ds["topk_w"],
+                                        ds["shared_out"], ds["residual"], ds["gamma"], ds["eps"],
+                                        ds["scale"], want_exact=False)
+                runs.append(time.perf_counter() - t1)
+            med = sorted(runs)[1]
+            nb = synth.algorithmic_bytes(ds["perm_idx"], ds["H"], ds["K"])
+            small[f"{cfg}_T{T}"] = {"us_per_call": round(med * 1e6, 1),
+                                    "gbs": round(nb / med / 1e9, 4)}
     finally:
         os.sched_setaffinity(0, allowed)
     cpu = "unknown"
@@ -272,7 +287,8 @@ def cpu_baseline(d, min_seconds=10.0, max_passes=20):
             "kind": "oracle",
             "sample": f"the whole {d['T']}-token workload, {passes} passes, single thread pinned to "
                       f"core {core} ({dt:.1f} s; {dt / passes * 1e6:.0f} µs/call; host: {cpu}, "
-                      f"{len(allowed)} of {os.cpu_count()} logical CPUs available)"}
+                      f"{len(allowed)} of {os.cpu_count()} logical CPUs available)",
+            "smaller_workloads": small}
 
 
 def traffic_for_headline():
