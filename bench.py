@@ -20,7 +20,8 @@ Modes used with rocprofv3 (see profiles/):
   --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
                      size, for counter collection (FETCH_SIZE / WRITE_SIZE)
   --latency-run      eager calls at the decode sizes and the 512 batch (and the
-                     dense op at T=28 and 8192), to trace
+                     dense, FP8-output and dense FP8-output calls at T=28 and
+                     8192), to trace
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
   --pmc-variants-run the dense tail, the FP8-output call and the dense tail with
@@ -650,7 +651,8 @@ def run_latency(args):
     """Eager calls for a kernel trace, small sizes first so that no large call
     has flushed the caches before them: the fused op at the decode sizes, the
     FP8-output call and the dense tail at T = 28, the 512-token batch, then
-    the dense tail and the FP8-output call at T = 8192."""
+    the dense tail and the FP8-output call at T = 8192, and last the dense
+    tail with FP8 output at T = 28 and 8192."""
     import torch
     import synth
     torch.cuda.set_device(0)
@@ -671,6 +673,10 @@ def run_latency(args):
     run(make_dense_caller(synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192))),
         20, "dense T=8192")
     run(stacked_calls(synth.config_inputs("prefill", 8192), 1, "fp8")[0], 20, "fp8 output T=8192")
+    run(_dense_fp8_caller(synth.dense_inputs(28, 6144, seed=synth.seed_for("prefill", 28))),
+        args.steps, "dense fp8 output T=28")
+    run(_dense_fp8_caller(synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192))),
+        20, "dense fp8 output T=8192")
 
 
 def run_bench(args):
