@@ -22,10 +22,11 @@
 //     before the first FMA (gathering the routes together keeps K rows in
 //     flight per thread);
 //   * FP32 FMA chain in slot order in VGPRs; s = (routed + shared) + residual;
-//     residual_out is stored at once;
 //   * sum of squares: per lane, then a DPP tree within each wave, then one
 //     LDS step across waves behind a single barrier;
-//   * normalisation from the registers still holding s (no second read).
+//   * after the barrier, residual_out = bf16(s) (before it, in the dense bf16
+//     tail) and the normalisation, both from the registers still holding s
+//     (no second read).
 // Two launch shapes ("paths") of the same kernel:
 //   * token path (small T, latency): the widest workgroup, one 16-byte vector
 //     per thread per row (768 threads at H = 6144), so the K row loads of a
@@ -208,9 +209,14 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
             buf_store_u32<kAuxDefault>(1u, make_rsrc(p.bad_index, 4u), 0u);
     }
 
-    // s = (routed + shared) + residual (dense: x + residual); residual_out =
-    // bf16(s); per-lane sum of squares, and (FP8 modes) sg = s * gamma with its
-    // per-lane max |sg|.
+    // s = (routed + shared) + residual (dense: x + residual); per-lane sum of
+    // squares, and (FP8 modes) sg = s * gamma with its per-lane max |sg|. s
+    // stays in registers. residual_out = bf16(s) is stored after the barrier,
+    // next to the normalised output, which keeps the stores off the path to
+    // the barrier; the dense tail with bf16 output, half of whose bytes are
+    // writes, stores it before the barrier instead (each choice measured the
+    // faster for its variant on MI355X).
+    constexpr bool EARLY_RO = DENSE && QM == kOutBf16;
     const rsrc_t ro_r = make_rsrc(p.residual_out + trow, rowbytes);
     float ss = 0.0f;
     float mg = 0.0f;
@@ -229,12 +235,14 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
                 mg = __builtin_fmaxf(mg, __builtin_fabsf(sg[j][e]));
             }
         }
-        u32x4 o;
-        o.x = pack_bf16x2(acc[j][0], acc[j][1]);
-        o.y = pack_bf16x2(acc[j][2], acc[j][3]);
-        o.z = pack_bf16x2(acc[j][4], acc[j][5]);
-        o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-        buf_store<OUT_AUX>(o, ro_r, off[j]);
+        if constexpr (EARLY_RO) {
+            u32x4 o;
+            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+            buf_store<OUT_AUX>(o, ro_r, off[j]);
+        }
     }
 
     // Row reduction: wave tree, then the waves' partial sums in order. The FP8
@@ -269,6 +277,19 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
 #pragma unroll
     for (int w = MAX_WAVES; w < NRED; ++w) rmg = __builtin_fmaxf(rmg, part[w]);
     const float rstd = rsqrt_f32(tot / p.h_f + p.eps);
+
+    // residual_out = bf16(s), one rounding
+    if constexpr (!EARLY_RO) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            u32x4 o;
+            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+            buf_store<OUT_AUX>(o, ro_r, off[j]);
+        }
+    }
 
     if (QM != kOutFp8) {
         const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
