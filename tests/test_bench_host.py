@@ -202,3 +202,15 @@ def test_rate_units():
     # 1,208,496,128 bytes in 195 µs is 6197.4 GB/s, 77.47% of 8 TB/s
     r = bench._rate(195.0, 1208496128)
     assert r == {"us": 195.0, "gbs": 6197.4, "frac": 0.7747}
+
+
+def test_more_than_one_gpu_is_refused():
+    """The bench measures one GPU: --gpus above 1 (or a multi-rank launch)
+    exits with status 2 and says why, before touching a GPU."""
+    import subprocess
+    import sys
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args, cwd=ROOT,
+                           env=dict(os.environ, **env), capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "measures one GPU" in r.stderr and r.stdout == ""
