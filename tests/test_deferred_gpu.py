@@ -140,6 +140,56 @@ def test_decoder_tail_graph_replay():
         assert np.array_equal(gu.host_u16(h_g), want_h), i
 
 
+def test_decoder_tail_graph_replay_fp8():
+    """The same two boundaries with FP8 outputs, as in a model whose
+    projections run in FP8: the post-attention norm and the next layer's input
+    norm both write E4M3 codes and per-token scales. Captured once, replayed
+    many times, every replay bit-identical to eager."""
+    T, H, K = 28, 6144, 8
+    d = synth.generate(T, H, K, scale=2.5, seed=74)
+    dd, u = _dev(d)
+    attn_out = gu.dev_bf16(synth.dense_inputs(T, H, seed=75)["x"])
+    res0 = dd["residual"].clone()
+    g1, g2 = dd["gamma"], gu.dev_bf16(synth.dense_inputs(T, H, seed=76)["gamma"])
+    outs = [(torch.empty((T, H), dtype=torch.float8_e4m3fn, device="cuda"),
+             torch.empty((T,), dtype=torch.float32, device="cuda")) for _ in range(2)]
+
+    def step(res):
+        mfr.fused_add_rmsnorm(attn_out, res, g1, d["eps"], in_place=True, fp8=True,
+                              normed_fp8=outs[0][0], fp8_scale=outs[0][1])
+        mfr.fused_add_rmsnorm(mfr.MoEOutput(u, dd["shared_out"]), res, g2, d["eps"],
+                              in_place=True, fp8=True, normed_fp8=outs[1][0],
+                              fp8_scale=outs[1][1])
+
+    def snapshot(res):
+        return [res.view(torch.int16).clone()] + [t.view(torch.uint8).clone() for q, sc in outs
+                                                   for t in (q, sc.view(torch.uint8))]
+    res_e = res0.clone()
+    step(res_e)
+    torch.cuda.synchronize()
+    want = snapshot(res_e)
+
+    res_g = res0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(res_g.clone())
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(res_g)
+    for i in range(10):
+        res_g.copy_(res0)
+        for q, sc in outs:
+            q.view(torch.uint8).zero_()
+            sc.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot(res_g)
+        assert all(torch.equal(a, b) for a, b in zip(got, want)), i
+
+
 @pytest.mark.parametrize("in_place", [False, True], ids=["separate", "in_place"])
 @pytest.mark.parametrize("deferred", [True, False], ids=["moe", "dense"])
 def test_fp8_consumer_equals_direct_calls(deferred, in_place):
