@@ -10,8 +10,8 @@ Source of the definitions: vLLM pull request #62174 (deferred MoE finalize for
 GLM-5.x), sections Details and Validation, for finalize_rmsnorm; "Port the
 validated GLM-5.2 H200 production path to latest vLLM", Ported behavior, for
 the dense residual_rmsnorm, and Prepared experiment branches (dynamic
-per-token FP8 activations) for fp8_quantize_rows. The header of ``mfr_oracle.cpp`` lists the readings
-taken where the pages are silent.
+per-token FP8 activations) for fp8_quantize_rows. The header of
+``mfr_oracle.cpp`` lists the readings taken where the pages are silent.
 
 Parity pins: every function here is pinned by tests/test_oracle.py (hand cases,
 closed forms, invariants, library special cases, exact brute force); none is
