@@ -1,8 +1,9 @@
 """Host logic of bench.py that the committed profiles come from, on synthetic
-rocprofv3 CSVs with known answers (CPU only): the kernel-trace summary
-(mean, median, p10, p90), the FETCH_SIZE / WRITE_SIZE calibration against
-the 1 GiB copy probe, the join of the shader and L2 counter passes, the code-hash gate on roofline.traffic, and the byte
-count of the headline workload."""
+rocprofv3 CSVs with known answers (CPU only): the kernel-trace summary (mean,
+median, p10, p90), the FETCH_SIZE / WRITE_SIZE calibration against the 1 GiB
+copy probe, the join of the shader and L2 counter passes, the code-hash gate on
+roofline.traffic, the byte counts of the workloads, and the refusal of more
+than one GPU."""
 import argparse
 import csv
 import json

@@ -880,7 +880,9 @@ const char* moe_finalize_rmsnorm_strerror(int status) {
     switch (status) {
         case MFR_OK: return "success";
         case MFR_ERR_NULL: return "a required pointer is NULL";
-        case MFR_ERR_SHAPE: return "T, H or K outside the supported limits (0<=T<2^31, 8<=H<=16384, H%8==0, 1<=K<=16)";
+        case MFR_ERR_SHAPE:
+            return "T, H or K outside the supported limits "
+                   "(0<=T<2^31, 8<=H<=16384, H%8==0, 1<=K<=16)";
         case MFR_ERR_ALIGN: return "bf16 pointers must be 16-byte aligned, perm_idx/topk_w 4-byte aligned";
         case MFR_ERR_ALIAS: return "an output overlaps an input or the other output (only residual_out == residual is allowed)";
         case MFR_ERR_SCALAR: return "eps must be finite and >= 0, scale must be finite";
