@@ -10,7 +10,8 @@ timed region; HIP events on the launch stream bracket exactly --steps calls.
 
 Printed (stdout, one JSON line): effective HBM GB/s = algorithmic bytes per
 call / time per call, the roofline object for the fused kernel, the oracle's
-CPU baseline on the same workload, and, as context, decode-latency figures for
+CPU baseline on the same workload (one core, and every core in threads over
+disjoint token ranges), and, as context, decode-latency figures for
 T = 1..64 and the 512-token batch, a measured copy ceiling, the dense tail and
 the FP8-output calls at T = 8192, the host cost of the torch deferred path, and
 the headline workload with its gathered rows grouped by expert instead of
@@ -284,12 +285,43 @@ def cpu_baseline(d, min_seconds=10.0, max_passes=20):
                     break
     except OSError:
         pass
+    all_cores = cpu_baseline_all_cores(d, nbytes)
     return {"value": round(nbytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "all_cores": all_cores,
             "sample": f"the whole {d['T']}-token workload, {passes} passes, single thread pinned to "
                       f"core {core} ({dt:.1f} s; {dt / passes * 1e6:.0f} µs/call; host: {cpu}, "
                       f"{len(allowed)} of {os.cpu_count()} logical CPUs available)",
             "smaller_workloads": small}
+
+
+def cpu_baseline_all_cores(d, nbytes, min_seconds=5.0, max_passes=50):
+    """The same oracle routine on every core the process may use: one thread
+    per core, each evaluating a disjoint, contiguous range of tokens (the
+    oracle is per token, and its C entry point runs without the interpreter
+    lock). Whole passes over the workload are repeated until at least
+    min_seconds of wall time."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    n = len(os.sched_getaffinity(0))
+    T = d["T"]
+    bounds = [(T * i // n, T * (i + 1) // n) for i in range(n)]
+
+    def part(b):
+        t0, t1 = b
+        oracle.finalize_rmsnorm(d["expert_out"], d["perm_idx"][t0:t1], d["topk_w"][t0:t1],
+                                d["shared_out"][t0:t1], d["residual"][t0:t1], d["gamma"],
+                                d["eps"], d["scale"], want_exact=False)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(part, bounds))  # warm-up pass
+        t0 = time.perf_counter()
+        passes = 0
+        while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+            list(ex.map(part, bounds))
+            passes += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": n,
+            "sample": f"the whole {T}-token workload, {passes} passes, {n} threads over disjoint "
+                      f"token ranges ({dt:.1f} s wall; {dt / passes * 1e6:.0f} µs/call)"}
 
 
 def traffic_for_headline():
@@ -481,18 +513,22 @@ def producer_written_us(d, n=64):
     return round(t_pair - t_prod, 2)
 
 
-def graph_ceiling_batch():
+def graph_ceiling_batch(reps=3):
     """The 512-token batch (H=6144, K=8): HBM-cold (a graph cycling over 8
-    buffer sets, 604 MB > Infinity Cache) and cache-warm (one set)."""
+    buffer sets, 604 MB > Infinity Cache) and cache-warm (one set). The cold
+    figure is the median of reps timings (each 5 replays of 64 calls); their
+    range is reported beside it."""
     import synth
     d = synth.config_inputs("batch512", 512)
     nbytes = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
     sets = [to_device(d) for _ in range(8)]
     calls = [make_caller(dd, d["eps"], d["scale"])[0] for dd in sets]
-    cold = time_graph(calls, 8, 5) * 1e3
+    colds = sorted(time_graph(calls, 8, 5) * 1e3 for _ in range(reps))
+    cold = colds[len(colds) // 2]
     warm = time_graph(calls[:1], 64, 5) * 1e3
     return {"us_cold": round(cold, 2), "gbs_cold": round(nbytes / (cold * 1e-6) / 1e9, 1),
             "frac_cold": round(nbytes / (cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "us_cold_range": [round(colds[0], 2), round(colds[-1], 2)], "reps": reps,
             "us_warm": round(warm, 2), "bytes": nbytes}
 
 

@@ -9,6 +9,7 @@ import csv
 import json
 import os
 
+import numpy as np
 import pytest
 
 import bench
@@ -215,3 +216,27 @@ def test_more_than_one_gpu_is_refused():
                            env=dict(os.environ, **env), capture_output=True, text=True, timeout=120)
         assert r.returncode == 2, r.stderr
         assert "measures one GPU" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_all_cores_covers_every_token(monkeypatch):
+    """The all-cores oracle leg splits the tokens into disjoint ranges that
+    together cover the workload once per pass, one thread per allowed core."""
+    import oracle
+    d = synth.config_inputs("tiny", 4)
+    seen = []
+    real = oracle.finalize_rmsnorm
+
+    def spy(expert_out, perm_idx, *a, **kw):
+        seen.append(perm_idx.copy())
+        return real(expert_out, perm_idx, *a, **kw)
+    monkeypatch.setattr(oracle, "finalize_rmsnorm", spy)
+    nb = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+    r = bench.cpu_baseline_all_cores(d, nb, min_seconds=0.0, max_passes=1)
+    n = len(os.sched_getaffinity(0))
+    assert r["cores"] == n and r["value"] > 0 and r["unit"] == "GB/s"
+    # a warm-up pass, then one timed pass, each of the n ranges (in any order)
+    assert len(seen) == 2 * n
+    for p in range(2):
+        got = np.concatenate([s for s in seen[p * n:(p + 1) * n] if s.size], axis=0)
+        assert np.array_equal(np.sort(got, axis=None), np.sort(d["perm_idx"], axis=None))
+        assert got.shape == d["perm_idx"].shape
