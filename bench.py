@@ -55,10 +55,9 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def _elf_section(path, name):
-    """Bytes of one section of a 64-bit little-endian ELF file, or None."""
-    with open(path, "rb") as f:
-        b = f.read()
+def _elf_sections(b):
+    """{name: bytes} of the sections of a 64-bit little-endian ELF image
+    (NOBITS sections map to b""), or None if b is not one."""
     if b[:4] != b"\x7fELF" or b[4] != 2 or b[5] != 1:
         return None
     shoff, = struct.unpack_from("<Q", b, 0x28)
@@ -68,21 +67,66 @@ def _elf_section(path, name):
         return struct.unpack_from("<IIQQQQIIQQ", b, shoff + i * shentsize)
     strtab = header(shstrndx)
     names = b[strtab[4]:strtab[4] + strtab[5]]
+    out = {}
     for i in range(shnum):
         h = header(i)
-        if names[h[0]:names.index(b"\0", h[0])].decode() == name:
-            return b[h[4]:h[4] + h[5]]
-    return None
+        name = names[h[0]:names.index(b"\0", h[0])].decode()
+        out[name] = b"" if h[1] == 8 else b[h[4]:h[4] + h[5]]
+    return out
 
 
-def kernel_code_hash():
-    """Hash of the gfx950 code objects embedded in the built library (the
-    .hip_fatbin section): it changes exactly when the kernels' machine code
-    does, and not for host-only edits. Traffic figures measured on other
-    kernel code are not reported."""
-    from top_finalize_residual_amd import build as b
-    sec = _elf_section(b.LIB, ".hip_fatbin") if os.path.exists(b.LIB) else None
-    return hashlib.sha256(sec).hexdigest()[:16] if sec else None
+def _offload_bundle(b):
+    """[(target triple, code object bytes)] of an uncompressed clang offload
+    bundle (the .hip_fatbin section of a HIP library)."""
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    if b[:len(magic)] != magic:
+        return None
+    n, = struct.unpack_from("<Q", b, len(magic))
+    off, out = len(magic) + 8, []
+    for _ in range(n):
+        o, size, tl = struct.unpack_from("<QQQ", b, off)
+        off += 24
+        out.append((b[off:off + tl].decode(), b[o:o + size]))
+        off += tl
+    return out
+
+
+# Sections of a gfx950 code object that hold the kernels' machine code, their
+# descriptors and their metadata. The symbol tables are left out: they name a
+# per-build identifier derived from the build path.
+CODE_SECTIONS = (".text", ".rodata", ".note")
+
+
+def kernel_code_hash(lib_path=None):
+    """Hash of the machine code of the gfx950 kernels in a built library: the
+    .text, .rodata and .note sections of every gfx950 code object in its
+    offload bundle. It changes when the kernels' code, resources or
+    metadata change, and is the same for the same source built at any path.
+    Traffic figures measured on other kernel code are not reported."""
+    if lib_path is None:
+        from top_finalize_residual_amd import build as bld
+        lib_path = bld.LIB
+    if not os.path.exists(lib_path):
+        return None
+    with open(lib_path, "rb") as f:
+        host = _elf_sections(f.read())
+    bundle = _offload_bundle(host.get(".hip_fatbin", b"")) if host else None
+    if not bundle:
+        return None
+    h = hashlib.sha256()
+    found = False
+    for triple, co in bundle:
+        if "gfx950" not in triple:
+            continue
+        secs = _elf_sections(co)
+        if secs is None:
+            return None
+        found = True
+        h.update(triple.encode())
+        for name in CODE_SECTIONS:
+            data = secs.get(name, b"")
+            h.update(name.encode() + struct.pack("<Q", len(data)) + data)
+    return h.hexdigest()[:16] if found else None
 
 
 # ---------------------------------------------------------------------------
@@ -661,8 +705,10 @@ def _rate(us, nbytes):
 
 def deferred_overhead():
     """Host cost of the torch-facing deferred path at one decode step (T=28):
-    eager calls through fused_add_rmsnorm (custom op dispatch + ctypes) and
-    through the raw C call, against the same call replayed from a graph."""
+    eager calls of fused_add_rmsnorm (the public consumer norm; with plain
+    tensors it runs the op's kernel without the dispatcher), of the same op
+    through torch.ops (the dispatcher, as under torch.compile), and of the raw
+    C call, against the call replayed from a graph."""
     import torch
     import synth
     import top_finalize_residual_amd as mfr
@@ -671,16 +717,29 @@ def deferred_overhead():
     u = mfr.UnfinalizedMoEOutput(dd["expert_out"], dd["perm_idx"], dd["topk_w"], d["scale"])
     mo = mfr.MoEOutput(u, dd["shared_out"])
     ro, no = torch.empty_like(dd["residual"]), torch.empty_like(dd["residual"])
+    op = torch.ops.mfr.moe_finalize_rmsnorm.default
+    args = (dd["expert_out"], dd["perm_idx"], dd["topk_w"], dd["shared_out"], dd["residual"],
+            dd["gamma"], d["eps"], d["scale"], ro, no)
 
-    def via_op():
+    def via_public():
         mfr.fused_add_rmsnorm(mo, dd["residual"], dd["gamma"], d["eps"], residual_out=ro,
                               normed_out=no)
+
+    def via_torch_ops():
+        op(*args)
     raw, _ = make_caller(dd, d["eps"], d["scale"])
-    eager_op = round(time_calls([via_op], 300, 30) * 1e3, 2)
-    eager_raw = round(time_calls([raw], 300, 30) * 1e3, 2)
+    out = {"T": 28}
+    # interleaved, 3 rounds, median of each
+    runs = {"eager_op_us": [], "torch_ops_us": [], "eager_raw_us": []}
+    for _ in range(3):
+        runs["eager_op_us"].append(time_calls([via_public], 300, 30) * 1e3)
+        runs["torch_ops_us"].append(time_calls([via_torch_ops], 300, 30) * 1e3)
+        runs["eager_raw_us"].append(time_calls([raw], 300, 30) * 1e3)
+    for k, v in runs.items():
+        out[k] = round(sorted(v)[1], 2)
     scrub_infinity_cache()  # the cache state of decode_latency's same_inputs
-    return {"T": 28, "eager_op_us": eager_op, "eager_raw_us": eager_raw,
-            "graph_op_us": round(time_graph([via_op], 100, 5) * 1e3, 2)}
+    out["graph_op_us"] = round(time_graph([via_public], 100, 5) * 1e3, 2)
+    return out
 
 
 def run_latency(args):

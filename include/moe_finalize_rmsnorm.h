@@ -30,7 +30,6 @@
  *   residual_add_rmsnorm_fp8          the dense tail with FP8 output
  *   moe_finalize_rmsnorm_path         host-only: the launch path of a shape
  *   moe_finalize_rmsnorm_strerror     text of a status code
- *   moe_finalize_rmsnorm_force        process-wide launch override (testing)
  *
  * Data types and layout (all row-major, contiguous, device memory):
  *   bf16 tensors are passed as raw 16-bit patterns (uint16_t).
@@ -55,6 +54,16 @@
  *   residual_out [T, H]  bf16   output; may be exactly equal to residual
  *                               (in place), must not overlap anything else
  *   normed_out   [T, H]  bf16   output; must not overlap any other argument
+ *
+ * Range: s is accumulated in fp32, as the page's kernel accumulates (Claims),
+ * so |s| must stay below 2^128 (the fp32 range; an overflowing s gives an
+ * infinite residual_out on both the fused and the unfused chain, and a NaN or
+ * zero normed row). Within that range every finite row is normalised: rows
+ * whose fp32 sum of squares overflows (|s| above about 2^64 / sqrt(H)) or is
+ * too small to use (mean(s^2) + eps below 2^-100, e.g. eps = 0 with
+ * subnormal s) are normalised again with an fp64 sum of squares, by the same
+ * kernel, at no cost to other rows. An all-zero row with eps = 0 gives NaN
+ * (0 / 0); an infinite or NaN s propagates (inf / inf = NaN, others 0).
  *
  * Limits: 0 <= T <= 2^31-1, 8 <= H <= 16384 with H % 8 == 0, 1 <= K <= 16.
  * bf16 pointers must be 16-byte aligned; perm_idx and topk_w 4-byte aligned.
@@ -95,7 +104,7 @@ enum mfr_status {
     MFR_ERR_ALIAS = 4,  /* outputs overlap inputs or each other (other than residual_out == residual) */
     MFR_ERR_SCALAR = 5, /* eps < 0, or eps or scale not finite */
     MFR_ERR_HIP = 6,    /* the HIP runtime refused the launch */
-    MFR_ERR_ARG = 7     /* an invalid value passed to moe_finalize_rmsnorm_force */
+    MFR_ERR_ARG = 7     /* an invalid launch override (the library's tuning interface) */
 };
 
 /* Both paths launch one workgroup per token (grid = T); they differ in launch
@@ -105,12 +114,6 @@ enum mfr_path {
     MFR_PATH_TOKEN = 1,  /* small T, latency: widest workgroup per token (768 threads at H = 6144) */
     MFR_PATH_STREAM = 2  /* large T, bandwidth: 256 threads per token, write-through stores once
                             the outputs outgrow the L2 */
-};
-
-enum mfr_store_policy {
-    MFR_STORE_AUTO = 0,
-    MFR_STORE_WRITE_BACK = 1,
-    MFR_STORE_WRITE_THROUGH = 2
 };
 
 /* The fused op. Definition, layouts, limits and errors: see above. */
@@ -225,9 +228,10 @@ int residual_add_rmsnorm_fp8(const uint16_t* x, const uint16_t* residual, const 
                              uint8_t* normed_fp8, float* fp8_scale,
                              int64_t T, int64_t H, hipStream_t stream);
 
-/* Which path moe_finalize_rmsnorm would take for this shape, taking any
- * override from moe_finalize_rmsnorm_force into account; MFR_PATH_UNSUPPORTED
- * if the shape is outside the limits. Pure host function: no HIP call. A
+/* Which path moe_finalize_rmsnorm would take for this shape from the calling
+ * thread (the MFR_PATH environment variable, read once at load, and a launch
+ * override of the library's tuning interface are taken into account);
+ * MFR_PATH_UNSUPPORTED if the shape is outside the limits. Pure host function: no HIP call. A
  * caller can use it to decide, before deferring its finalize, that the fused
  * op will accept the shape (the page's layers defer only when the fused kernel
  * will run: Details). T == 0 reports the path a nonzero T would take. */
@@ -235,17 +239,6 @@ int moe_finalize_rmsnorm_path(int64_t T, int64_t H, int64_t K);
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* moe_finalize_rmsnorm_strerror(int status);
-
-/* Process-wide launch override for testing and tuning; affects later calls
- * from every thread. path: 0 = automatic, MFR_PATH_TOKEN or MFR_PATH_STREAM.
- * vectors_per_thread: 0 = automatic, else 1..4 (16-byte vectors of each row
- * handled per thread; the workgroup size follows from H; a value whose
- * workgroup would exceed the kernel's limit falls back to automatic).
- * store_policy: an mfr_store_policy value. residual_out is bit-identical
- * under every override; normed_out can differ in the last bit between
- * workgroup shapes, whose sum-of-squares reduction trees differ. Returns
- * MFR_ERR_ARG for values outside those ranges (nothing changes). */
-int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int store_policy);
 
 #ifdef __cplusplus
 }

@@ -8,11 +8,15 @@ plus an ulp distance of at most 1 from the oracle's own bf16 output wherever
 |ref| >= 2^-8. Below that the absolute term governs: the fp32 sum carries an
 absolute error of order 2^-24 times the magnitude of its addends (about 1e-6
 here), which near a cancellation spans many bf16 ulps of the tiny result."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
 import oracle
 import top_finalize_residual_amd as mfr
+from top_finalize_residual_amd import tuning
 
 REL = 2.0 ** -8
 ABS = 1e-6
@@ -36,27 +40,34 @@ def to_device(d):
                 gamma=dev_bf16(d["gamma"]))
 
 
-class forced:
-    """Context manager: force a launch configuration, restore automatic after."""
-
-    def __init__(self, path=0, vpt=0, store=0):
-        self.args = (path, vpt, store)
-
-    def __enter__(self):
-        mfr.moe_finalize_rmsnorm_force(*self.args)
-        return self
-
-    def __exit__(self, *exc):
-        mfr.moe_finalize_rmsnorm_force(0, 0, 0)
-        return False
+forced = tuning.forced  # force a launch configuration on this thread, automatic after
 
 
-def run(dd, eps, scale, path=0, vpt=0, store=0, residual_out=None, normed_out=None):
-    """One call on device tensors; returns host uint16 (residual_out, normed_out)."""
+def run(dd, eps, scale, path=0, vpt=0, store=0, residual_out=None, normed_out=None, api="c"):
+    """One call on device tensors; returns host uint16 (residual_out, normed_out).
+
+    api="c": the plain C entry point moe_finalize_rmsnorm on the tensors'
+    addresses (the call the benchmark times); api="binding": the tensor-level
+    binding, which goes through the checked entry point with R =
+    expert_out.shape[0]."""
     with forced(path, vpt, store):
-        r, n = mfr.moe_finalize_rmsnorm(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
-                                        dd["shared_out"], dd["residual"], dd["gamma"], eps, scale,
-                                        residual_out=residual_out, normed_out=normed_out)
+        if api == "binding":
+            r, n = mfr.moe_finalize_rmsnorm(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
+                                            dd["shared_out"], dd["residual"], dd["gamma"], eps,
+                                            scale, residual_out=residual_out,
+                                            normed_out=normed_out)
+        else:
+            T, K = dd["perm_idx"].shape
+            H = dd["gamma"].shape[0]
+            r = torch.empty_like(dd["residual"]) if residual_out is None else residual_out
+            n = torch.empty_like(dd["residual"]) if normed_out is None else normed_out
+            rc = mfr.moe_finalize_rmsnorm_raw(
+                *(dd[k].data_ptr() for k in ("expert_out", "perm_idx", "topk_w", "shared_out",
+                                             "residual", "gamma")),
+                eps, scale, r.data_ptr(), n.data_ptr(), T, H, K,
+                torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise mfr.MFRError(rc)
     torch.cuda.synchronize()
     return host_u16(r), host_u16(n)
 
@@ -110,3 +121,41 @@ def check(d, res_u16, nrm_u16, tokens=None, ref=None):
     assert_gate(res_u16, ref["s"], ref["residual_out"], "residual_out")
     assert_gate(nrm_u16, ref["normed_exact"], ref["normed_out"], "normed_out")
     return ref
+
+
+def _workers():
+    # the oracle's C entry point runs without the interpreter lock, so threads
+    # over disjoint token ranges use every core given to the process (at most
+    # 16, the CPU share of a one-GPU machine)
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_chunks(T, evaluate, chunk=1024):
+    """Yield (t0, t1, ref) over the tokens [0, T) in chunks, where ref is
+    evaluate(a, b) (an oracle call on tokens [a, b), returning a dict of
+    per-token arrays) computed in threads over disjoint sub-ranges of the
+    chunk and joined in token order. Bounded memory at any T."""
+    n = _workers()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        for t0 in range(0, T, chunk):
+            t1 = min(T, t0 + chunk)
+            bounds = [(t0 + (t1 - t0) * i // n, t0 + (t1 - t0) * (i + 1) // n) for i in range(n)]
+            bounds = [b for b in bounds if b[1] > b[0]]
+            parts = list(ex.map(lambda b: evaluate(*b), bounds))
+            yield t0, t1, {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+
+
+def finalize_evaluator(d):
+    """evaluate(a, b) for oracle_chunks: the oracle's fused op on tokens [a, b)."""
+    def evaluate(a, b):
+        return oracle.finalize_rmsnorm(d["expert_out"], d["perm_idx"][a:b], d["topk_w"][a:b],
+                                       d["shared_out"][a:b], d["residual"][a:b], d["gamma"],
+                                       d["eps"], d["scale"])
+    return evaluate
+
+
+def check_all_tokens(d, res_u16, nrm_u16, chunk=1024):
+    """check() over every token of a large call, the oracle run in threads
+    over token ranges."""
+    for t0, t1, ref in oracle_chunks(d["perm_idx"].shape[0], finalize_evaluator(d), chunk):
+        check(d, res_u16[t0:t1], nrm_u16[t0:t1], ref=ref)

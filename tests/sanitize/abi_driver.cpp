@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <limits>
 
+#include "mfr_tuning.h"
 #include "moe_finalize_rmsnorm.h"
 
 static int failures = 0;
@@ -45,12 +46,12 @@ int main() {
     expect(moe_finalize_rmsnorm_path(-1, 6144, 8), MFR_PATH_UNSUPPORTED, "path T < 0");
     for (int c = -1; c <= 8; ++c)
         if (!moe_finalize_rmsnorm_strerror(c)) expect(0, 1, "strerror returns text");
-    expect(moe_finalize_rmsnorm_force(3, 0, 0), MFR_ERR_ARG, "force bad path");
-    expect(moe_finalize_rmsnorm_force(0, 5, 0), MFR_ERR_ARG, "force bad vpt");
-    expect(moe_finalize_rmsnorm_force(0, 0, 3), MFR_ERR_ARG, "force bad store");
-    expect(moe_finalize_rmsnorm_force(MFR_PATH_STREAM, 2, MFR_STORE_WRITE_THROUGH), MFR_OK, "force");
+    expect(mfr_tuning_force_launch(4, 0, 0), MFR_ERR_ARG, "force bad path");
+    expect(mfr_tuning_force_launch(0, 5, 0), MFR_ERR_ARG, "force bad vpt");
+    expect(mfr_tuning_force_launch(0, 0, 3), MFR_ERR_ARG, "force bad store");
+    expect(mfr_tuning_force_launch(MFR_PATH_STREAM, 2, MFR_STORE_WRITE_THROUGH), MFR_OK, "force");
     expect(moe_finalize_rmsnorm_path(1, 6144, 8), MFR_PATH_STREAM, "forced path");
-    expect(moe_finalize_rmsnorm_force(0, 0, 0), MFR_OK, "force reset");
+    expect(mfr_tuning_force_launch(0, 0, 0), MFR_OK, "force reset");
 
     // the fused op
     expect(moe_finalize_rmsnorm(E, P, W, S, R, G, 1e-6f, 1.f, RO, NO, 0, H, K, nullptr), MFR_OK,

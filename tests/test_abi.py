@@ -13,6 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 
 mfr = pytest.importorskip("top_finalize_residual_amd", reason="HIP library not built")
 from top_finalize_residual_amd import binding  # noqa: E402
+from top_finalize_residual_amd import tuning  # noqa: E402
 
 T, H, K = 4, 2048, 8
 A = 1 << 20  # fake, 16-byte aligned, never dereferenced addresses
@@ -34,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_path",
-                 "moe_finalize_rmsnorm_strerror", "moe_finalize_rmsnorm_force",
+                 "moe_finalize_rmsnorm_strerror",
                  "residual_add_rmsnorm", "moe_finalize_rmsnorm_fp8",
                  "moe_finalize_rmsnorm_checked", "residual_add_rmsnorm_fp8",
                  "moe_finalize_rmsnorm_fp8_checked"):
@@ -72,21 +73,38 @@ def test_path_query():
     assert mfr.moe_finalize_rmsnorm_path(4, 8, 1) != mfr.PATH_UNSUPPORTED
 
 
-def test_force_overrides_and_validates():
+def test_launch_override_validates_and_is_per_thread():
+    """The tuning interface's launch override: validated, and it belongs to
+    the calling thread, so another thread's calls keep the automatic shape."""
+    import threading
     try:
-        mfr.moe_finalize_rmsnorm_force(mfr.PATH_STREAM, 0, 0)
+        tuning.force_launch(mfr.PATH_STREAM, 0, 0)
         assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_STREAM
-        mfr.moe_finalize_rmsnorm_force(mfr.PATH_TOKEN, 2, 0)
+        tuning.force_launch(mfr.PATH_TOKEN, 2, 0)
         assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
-        for bad in ((3, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 3), (0, 0, -1)):
+        for bad in ((4, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 3), (0, 0, -1)):
             with pytest.raises(mfr.MFRError) as e:
-                mfr.moe_finalize_rmsnorm_force(*bad)
+                tuning.force_launch(*bad)
             assert e.value.status == binding.MFR_ERR_ARG
         # a rejected override leaves the previous one in place
         assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
+        seen = []
+        th = threading.Thread(target=lambda: seen.append(mfr.moe_finalize_rmsnorm_path(8192, 6144, 8)))
+        th.start()
+        th.join()
+        assert seen == [mfr.PATH_STREAM]  # the other thread is not overridden
     finally:
-        mfr.moe_finalize_rmsnorm_force(0, 0, 0)
+        tuning.force_launch(0, 0, 0)
     assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_STREAM
+
+
+def test_public_header_has_no_launch_override():
+    """The public header declares only the op's entry points: the launch
+    override lives in the library's internal tuning header."""
+    names = declared_functions()
+    assert not any("force" in n for n in names), names
+    text = open(os.path.join(INCLUDE, "moe_finalize_rmsnorm.h")).read()
+    assert "mfr_tuning" not in text and "MFR_STORE_" not in text
 
 
 def _ptrs(**over):
@@ -258,7 +276,7 @@ def _path_in_subprocess(env_value, T, forced=0):
             "from top_finalize_residual_amd import build\n"
             "lib = ctypes.CDLL(build.LIB)\n"
             "lib.moe_finalize_rmsnorm_path.argtypes = [ctypes.c_int64] * 3\n"
-            f"assert lib.moe_finalize_rmsnorm_force({forced}, 0, 0) == 0\n"
+            f"assert lib.mfr_tuning_force_launch({forced}, 0, 0) == 0\n"
             f"print(lib.moe_finalize_rmsnorm_path({T}, 6144, 8))\n")
     env = dict(os.environ)
     env.pop("MFR_PATH", None)
@@ -344,3 +362,41 @@ def test_fp8_checked_validation():
     # the optional outputs are not examined when absent
     assert fp8_checked_call(normed_out=None, bad_index=None, T_=0) == binding.MFR_OK
     assert fp8_checked_call(R=0, expert_out=None, T_=0) == binding.MFR_OK
+
+
+def test_launch_failure_is_reported_as_hip_error():
+    """A call that passes every host check and then cannot be launched
+    returns MFR_ERR_HIP, from every entry point. Without a GPU the HIP
+    runtime refuses the launch itself; the fake addresses below are never
+    dereferenced because nothing is enqueued. On a host with a GPU the
+    launches would run, so the test is skipped there (the GPU tests cover
+    real launches)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the calls would launch")
+    p = _ptrs()
+    lib = binding.lib()
+    ins = (p["expert_out"], p["perm_idx"], p["topk_w"], p["shared_out"], p["residual"], p["gamma"])
+    act = T * H * 2
+    q, sc, flag = A + 80 * act, A + 90 * act, A + 91 * act
+    calls = {
+        "moe_finalize_rmsnorm": lambda: lib.moe_finalize_rmsnorm(
+            *ins, 1e-6, 2.5, p["residual_out"], p["normed_out"], T, H, K, None),
+        "moe_finalize_rmsnorm_checked": lambda: lib.moe_finalize_rmsnorm_checked(
+            ins[0], T * K, *ins[1:], 1e-6, 2.5, p["residual_out"], p["normed_out"], flag, T, H, K,
+            None),
+        "moe_finalize_rmsnorm_fp8": lambda: lib.moe_finalize_rmsnorm_fp8(
+            *ins, 1e-6, 2.5, p["residual_out"], p["normed_out"], q, sc, T, H, K, None),
+        "moe_finalize_rmsnorm_fp8_checked": lambda: lib.moe_finalize_rmsnorm_fp8_checked(
+            ins[0], T * K, *ins[1:], 1e-6, 2.5, p["residual_out"], None, q, sc, flag, T, H, K,
+            None),
+        "residual_add_rmsnorm": lambda: lib.residual_add_rmsnorm(
+            p["shared_out"], p["residual"], p["gamma"], 1e-6, p["residual_out"], p["normed_out"],
+            T, H, None),
+        "residual_add_rmsnorm_fp8": lambda: lib.residual_add_rmsnorm_fp8(
+            p["shared_out"], p["residual"], p["gamma"], 1e-6, p["residual_out"], None, q, sc, T, H,
+            None),
+    }
+    for name, call in calls.items():
+        assert call() == binding.MFR_ERR_HIP, name
+    assert "HIP" in mfr.strerror(binding.MFR_ERR_HIP)

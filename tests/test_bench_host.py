@@ -93,12 +93,41 @@ def test_traffic_gate_follows_the_code_hash(tmp_path, monkeypatch):
 def test_code_hash_reads_the_embedded_code_objects(tmp_path):
     pytest.importorskip("top_finalize_residual_amd", reason="HIP library not built")
     from top_finalize_residual_amd import build as b
-    sec = bench._elf_section(b.LIB, ".hip_fatbin")
-    assert sec is not None and len(sec) > 0
-    assert bench.kernel_code_hash() == bench.kernel_code_hash()
+    with open(b.LIB, "rb") as f:
+        host = bench._elf_sections(f.read())
+    bundle = bench._offload_bundle(host[".hip_fatbin"])
+    assert any("gfx950" in triple for triple, _ in bundle)
+    assert bench.kernel_code_hash() == bench.kernel_code_hash() is not None
     not_elf = tmp_path / "x.so"
     not_elf.write_bytes(b"not an ELF file")
-    assert bench._elf_section(str(not_elf), ".hip_fatbin") is None
+    assert bench.kernel_code_hash(str(not_elf)) is None
+    assert bench._offload_bundle(b"something else") is None
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
+def test_code_hash_is_the_same_for_builds_at_different_paths(tmp_path):
+    """The same kernel source compiled in two directories (different source
+    and output paths, so different per-build identifiers in the symbol
+    tables) hashes the same, so a traffic record taken on one build is
+    recognised on another."""
+    import shutil
+    import subprocess
+    from top_finalize_residual_amd import build as b
+    procs, libs = [], []
+    for sub in ("a", os.path.join("b", "deeper")):
+        d = tmp_path / sub
+        shutil.copytree(b.CSRC, d / "csrc")
+        shutil.copytree(b.INCLUDE, d / "include")
+        lib = str(d / "libmoe_finalize_rmsnorm.so")
+        cmd = [b.HIPCC, *b.HIPFLAGS, *b.PRELOAD, "-I", str(d / "include"), "-I", str(d / "csrc"),
+               "-o", lib, str(d / "csrc" / "mfr_kernels.hip")]
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE))
+        libs.append(lib)
+    for p in procs:
+        _, err = p.communicate(timeout=600)
+        assert p.returncode == 0, err.decode()[-2000:]
+    h = [bench.kernel_code_hash(lib) for lib in libs]
+    assert h[0] is not None and h[0] == h[1]
 
 
 def test_closed_form_bytes_match_drawn_inputs():

@@ -7,6 +7,7 @@ import torch
 import oracle
 import synth
 import top_finalize_residual_amd as mfr
+from top_finalize_residual_amd import tuning
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -50,19 +51,24 @@ def test_dense_parity(T, H, path):
     assert np.array_equal(gu.bf16_f64(r[exact32]), gu.bf16_f64(ref["residual_out"][exact32]))
 
 
-def test_dense_prefill_full_size_sampled():
+def test_dense_prefill_full_size():
+    """The dense tail on an 8192-token chunk (1% of residual rows x100): every
+    token against the oracle (threads over token ranges)."""
     d = synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192), spike_frac=0.01)
     r, n = run_dense(d)
-    rng = np.random.default_rng(3)
-    tokens = np.sort(np.concatenate([d["spike_rows"], rng.choice(8192, 200, replace=False)]))
-    check_dense(d, r, n, tokens=np.unique(tokens))
+
+    def evaluate(a, b):
+        return oracle.residual_rmsnorm(d["x"][a:b], d["residual"][a:b], d["gamma"], d["eps"])
+    for t0, t1, ref in gu.oracle_chunks(8192, evaluate):
+        gu.assert_gate(r[t0:t1], ref["s"], ref["residual_out"], "residual_out")
+        gu.assert_gate(n[t0:t1], ref["normed_exact"], ref["normed_out"], "normed_out")
 
 
 @pytest.mark.parametrize("path", [mfr.PATH_TOKEN, mfr.PATH_STREAM], ids=["token", "stream"])
 def test_dense_in_place_and_store_policies(path):
     d = synth.dense_inputs(512, 6144, seed=8)
     r0, n0 = run_dense(d, path=path)
-    for store in (mfr.STORE_WRITE_BACK, mfr.STORE_WRITE_THROUGH):
+    for store in (tuning.STORE_WRITE_BACK, tuning.STORE_WRITE_THROUGH):
         r1, n1 = run_dense(d, path=path, store=store)
         assert np.array_equal(r0, r1) and np.array_equal(n0, n1)
     resid = gu.dev_bf16(d["residual"])
@@ -143,15 +149,19 @@ def test_dense_fp8_parity(T, H, path):
     assert np.array_equal(sc2, sc)
 
 
-def test_dense_fp8_prefill_full_size_sampled():
+def test_dense_fp8_prefill_full_size():
+    """The dense tail with FP8 output on an 8192-token chunk (1% of residual
+    rows x100): every token's codes, scale and residual_out against the
+    oracle (threads over token ranges)."""
     from tests.test_fp8_gpu import check_fp8
     d = synth.dense_inputs(8192, 6144, seed=synth.seed_for("prefill", 8192), spike_frac=0.01)
     r, q, sc, _ = run_dense_fp8(d, bf16_normed=False)
-    rng = np.random.default_rng(4)
-    tokens = np.unique(np.concatenate([d["spike_rows"], rng.choice(8192, 200, replace=False)]))
-    ref = oracle.residual_rmsnorm(d["x"][tokens], d["residual"][tokens], d["gamma"], d["eps"])
-    gu.assert_gate(r[tokens], ref["s"], ref["residual_out"], "residual_out")
-    check_fp8(q[tokens], sc[tokens], ref, d["gamma"], d["eps"])
+
+    def evaluate(a, b):
+        return oracle.residual_rmsnorm(d["x"][a:b], d["residual"][a:b], d["gamma"], d["eps"])
+    for t0, t1, ref in gu.oracle_chunks(8192, evaluate):
+        gu.assert_gate(r[t0:t1], ref["s"], ref["residual_out"], "residual_out")
+        check_fp8(q[t0:t1], sc[t0:t1], ref, d["gamma"], d["eps"])
 
 
 def test_dense_fp8_graph_replay():

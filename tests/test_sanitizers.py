@@ -53,7 +53,7 @@ def test_library_host_code_under_sanitizers(tmp_path):
           "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "mfr_kernels.hip"), "-o", obj],
          timeout=600)
     _run([CLANG, "-std=c++17", "-O1", "-g", *HOST_SAN, "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
-          "-I", "/opt/rocm/include", os.path.join(HERE, "abi_driver.cpp"), obj,
+          "-I", CSRC, "-I", "/opt/rocm/include", os.path.join(HERE, "abi_driver.cpp"), obj,
           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe], timeout=300)
     r = _run([exe], env=ENV, timeout=120)
     assert "abi driver: ok" in r.stdout

@@ -14,12 +14,9 @@ from .binding import (  # noqa: F401
     PATH_STREAM,
     PATH_TOKEN,
     PATH_UNSUPPORTED,
-    STORE_AUTO,
-    STORE_WRITE_BACK,
-    STORE_WRITE_THROUGH,
     moe_finalize_rmsnorm,
     moe_finalize_rmsnorm_checked,
-    moe_finalize_rmsnorm_force,
+    moe_finalize_rmsnorm_checked_raw,
     moe_finalize_rmsnorm_fp8,
     moe_finalize_rmsnorm_fp8_checked,
     moe_finalize_rmsnorm_fp8_checked_raw,

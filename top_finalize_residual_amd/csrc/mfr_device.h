@@ -80,17 +80,6 @@ __device__ __forceinline__ void buf_store_u32(uint32_t v, rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, AUX);
 }
 
-// 1 / sqrt(x) for x >= 0 through the hardware v_rsq_f32 (within 1 ulp; the
-// fp32 sum of squares feeding it already carries several). That instruction
-// treats a subnormal input as zero, so inputs below 2^-100 are scaled by 2^64
-// first and the result by 2^32 after, both exact. x = 0 gives +inf, +inf
-// gives 0, NaN stays NaN.
-__device__ __forceinline__ float rsqrt_f32(float x) {
-    const bool tiny = x < 0x1p-100f;
-    const float r = __builtin_amdgcn_rsqf(tiny ? x * 0x1p64f : x);
-    return tiny ? r * 0x1p32f : r;
-}
-
 // 448 / m for m > 0, made safe to scale by: the correctly rounded quotient,
 // lowered by one ulp where m times it rounds above 448. Rounding is monotone,
 // so |x| <= m then gives |x * factor| <= 448 after rounding, the largest
@@ -133,6 +122,33 @@ __device__ __forceinline__ float wave_sum(float x) {
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
     return (r0 + r1) + (r2 + r3);
+}
+
+// One DPP move of a double (its two halves moved alike).
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xF, 0xF, false);
+    const uint32_t hi =
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane64(double x, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u), lane);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// wave_sum in fp64: the same fixed tree, for the sum of squares taken when
+// the fp32 one leaves the fp32 range.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    x += dpp64<0xB1>(x);
+    x += dpp64<0x4E>(x);
+    x += dpp64<0x141>(x);
+    x += dpp64<0x140>(x);
+    return (readlane64(x, 0) + readlane64(x, 16)) + (readlane64(x, 32) + readlane64(x, 48));
 }
 
 // Maximum over the 64 lanes of a wave, returned to every lane; the same DPP

@@ -40,6 +40,7 @@
 // the hardware dispatcher balances the tail better than a static assignment.
 
 #include "mfr_device.h"
+#include "mfr_tuning.h"
 #include "moe_finalize_rmsnorm.h"
 
 #include <atomic>
@@ -79,6 +80,22 @@ constexpr float kE4m3Max = 448.0f;  // largest finite OCP E4M3 value
 
 constexpr int MAX_WAVES = 16;  // 1024 threads
 
+// Workgroup scratch in LDS: the per-wave partial results of the row
+// reductions.
+struct Lds {
+    float red[2 * MAX_WAVES];  // sums of squares, then (FP8 modes) maxima of |s * gamma|
+    double red64[MAX_WAVES];   // fp64 sums of squares (range rescue only)
+    float redm[MAX_WAVES];     // maxima of |y| (range rescue, FP8 modes)
+};
+
+// The fp32 normalisation is used when mean(s^2) + eps lies in
+// [kRescueBelow, FLT_MAX]. Above, the fp32 sum of squares has overflowed;
+// below, fp32 subnormal squares (or squares flushed to zero) could decide
+// rstd, which happens only with eps (nearly) 0. There the row is
+// normalised again in fp64.
+constexpr float kRescueBelow = 0x1p-100f;
+constexpr float kFltMax = 0x1.fffffep127f;
+
 // Routing metadata of slots [k0, k0 + 8): indices and weights, read
 // unconditionally (wave-uniform scalar loads, merged by the compiler). With
 // CHECK_K, slots at or past K re-read slot K-1 so every load stays in bounds;
@@ -95,39 +112,56 @@ __device__ __forceinline__ void load_meta8(const Params& p, const int32_t* prow,
     }
 }
 
-// Loads the rows of slots [k0, k0 + 8) and folds them into acc in slot order.
-// Straight-line code: all eight row loads are issued, then the FMAs. A masked
-// slot (index < 0), a slot whose index is at or past R, or a slot at or past
-// K gets a zero-record descriptor and a zero weight: its loads return zeros
-// without touching memory and its FMA adds +0, which leaves acc bit-for-bit
-// unchanged (acc starts at +0 and an exact-zero sum rounds to +0). No
-// branches. ROWS (the entry point told R) also masks an index at or past
-// the rows and, when the caller asked for the report, returns whether a slot
-// within K held one (the indices are wave-uniform, so the result is too);
-// without ROWS the code is the plain index >= 0 test.
+// Issues the row loads of slots [k0, k0 + 8): every load is in flight when
+// this returns, the rows in r and the scaled weights in w. A masked slot
+// (index < 0), a slot whose index is at or past R, or a slot at or past K
+// gets a zero-record descriptor and a zero weight: its loads return zeros
+// without touching memory, and its FMA in fold_rows8 adds +0, which leaves
+// acc bit-for-bit unchanged (acc starts at +0 and an exact-zero sum rounds to
+// +0). No branches. ROWS (the entry point told R) also masks an index at or
+// past the rows and, when the caller asked for the report, returns whether a
+// slot within K held one (the indices are wave-uniform, so the result is
+// too); without ROWS the code is the plain index >= 0 test. live = false
+// (the persistent path, a slot past the last token) gives every slot a
+// zero-record descriptor.
 template <int VPT, bool CHECK_K, bool ROWS>
-__device__ __forceinline__ bool gather_rows8(const Params& p, const int32_t (&idx)[8],
-                                             const float (&wr)[8], int k0,
-                                             const uint32_t (&off)[VPT], float (&acc)[VPT][8]) {
+__device__ __forceinline__ bool issue_rows8(const Params& p, const int32_t (&idx)[8],
+                                            const float (&wr)[8], int k0,
+                                            const uint32_t (&off)[VPT], u32x4 (&r)[8][VPT],
+                                            float (&w)[8], bool live = true) {
     const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
     rsrc_t rows[8];
-    float w[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
         // With ROWS, one unsigned compare masks both a negative index (it
         // wraps to 2^31 or more) and one at or past the rows.
         const bool in_range = ROWS ? static_cast<uint32_t>(idx[kk]) < p.rows : idx[kk] >= 0;
-        const bool use = in_range && (!CHECK_K || k0 + kk < p.K);
+        const bool use = live && in_range && (!CHECK_K || k0 + kk < p.K);
         rows[kk] = make_rsrc(p.expert_out + static_cast<int64_t>(use ? idx[kk] : 0) * p.V,
                              use ? rowbytes : 0u);
         const float ws = p.scale * wr[kk];
         w[kk] = use ? ws : 0.0f;
     }
-    u32x4 r[8][VPT];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
         for (int j = 0; j < VPT; ++j) r[kk][j] = buf_load<kAuxRows>(rows[kk], off[j]);
+    // Whether a slot within K held an index at or past the rows: only asked
+    // for when the caller wants the report (a uniform branch).
+    bool past_r = false;
+    if (ROWS && p.bad_index != nullptr) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            past_r |= live && (!CHECK_K || k0 + kk < p.K) && idx[kk] >= 0 &&
+                      static_cast<uint32_t>(idx[kk]) >= p.rows;
+    }
+    return past_r;
+}
+
+// Folds eight loaded rows into acc in slot order (an FMA chain per element).
+template <int VPT>
+__device__ __forceinline__ void fold_rows8(const u32x4 (&r)[8][VPT], const float (&w)[8],
+                                           float (&acc)[VPT][8]) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -135,79 +169,142 @@ __device__ __forceinline__ bool gather_rows8(const Params& p, const int32_t (&id
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 acc[j][e] = __builtin_fmaf(w[kk], vec_elem(r[kk][j], e), acc[j][e]);
-    // Whether a slot within K held an index at or past the rows: only asked
-    // for when the caller wants the report (a uniform branch).
-    bool past_r = false;
-    if (ROWS && p.bad_index != nullptr) {
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            past_r |= (!CHECK_K || k0 + kk < p.K) && idx[kk] >= 0 &&
-                      static_cast<uint32_t>(idx[kk]) >= p.rows;
-    }
+}
+
+// Loads the rows of slots [k0, k0 + 8) and folds them into acc in slot order.
+// Straight-line code: all eight row loads are issued, then the FMAs.
+template <int VPT, bool CHECK_K, bool ROWS>
+__device__ __forceinline__ bool gather_rows8(const Params& p, const int32_t (&idx)[8],
+                                             const float (&wr)[8], int k0,
+                                             const uint32_t (&off)[VPT], float (&acc)[VPT][8]) {
+    u32x4 r[8][VPT];
+    float w[8];
+    const bool past_r = issue_rows8<VPT, CHECK_K, ROWS>(p, idx, wr, k0, off, r, w);
+    fold_rows8<VPT>(r, w, acc);
     return past_r;
 }
 
-// One token, end to end. KT: 8 = exactly eight slots (the GLM-5.x / DeepSeek
-// top-8 case, no slot-count checks); 0 = any K in 1..16, as one or two
-// chunks of eight; -1 = no routed part (the dense residual add + RMSNorm:
-// shared_out holds x and s = x + residual). Thread i owns the byte offsets 16*(i + j*NT), j < VPT, of
-// every row; offsets at or past the row end (a ragged last tile) fall outside
-// the descriptors' range, so their loads return zero and their stores are
-// dropped by the hardware.
-template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS>
-__device__ __forceinline__ void finalize_token(const Params& p, const int64_t t, float* red) {
+// The normalisation of a row whose fp32 sum of squares cannot be used: it
+// overflowed (|s| beyond about 2^64 / sqrt(H), where rstd would come out 0
+// and the normed row as zeros), or it is so small that fp32 subnormal
+// squares, or squares flushed to zero, would decide rstd (eps near 0 and
+// |s| below about 2^-50; with eps = 0 and every square zero rstd would be
+// infinite). RMSNorm is defined on the exact sum (vLLM pull request #62174,
+// Validation: the fused result must match the unfused chain), and fp64 holds
+// the square of every fp32 value, so the squares are summed again in fp64,
+// in the same lane, wave and workgroup order, and rstd is taken in fp64.
+// rstd itself may lie outside the fp32 range, so it is split as
+// m * 2^k with m in [0.5, 1): y = ((s * 2^k) * m) * gamma in fp32, where
+// the scaling by 2^k is exact and |s * 2^k| stays below 2 sqrt(H). The
+// rounding steps are those of the fp32 path.
+// Entered by the whole workgroup or by none of it (the condition depends
+// only on the reduced sum, which every thread holds), so its barriers are
+// uniform. It adds no registers to the common path.
+// gamma is loaded again here rather than kept in registers past the
+// barrier, which the FP8-only output does not otherwise need.
+template <int VPT, int OUT_AUX, int QM>
+__device__ __forceinline__ void normalise_wide(const Params& p, const int64_t t,
+                                               const float (&acc)[VPT][8],
+                                               const uint32_t (&off)[VPT], Lds& lds) {
+    const int tid = threadIdx.x;
+    const int nw = blockDim.x >> 6;
+    const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
+    const int64_t trow = t * static_cast<int64_t>(p.V);
+    const rsrc_t gm_r = make_rsrc(p.gamma, rowbytes);
+    u32x4 gm[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) gm[j] = buf_load<kAuxGamma>(gm_r, off[j]);
+    // One element at a time (a scheduling barrier after each), so that only
+    // one converted value is live: this branch must not raise the register
+    // count of the kernel, and with it the occupancy of the common path.
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double v = acc[j][e];
+            ss = __builtin_fma(v, v, ss);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    const double wsum = wave_sum_f64(ss);
+    if ((tid & 63) == 0) lds.red64[tid >> 6] = wsum;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll 1
+    for (int w = 0; w < nw; ++w) tot += lds.red64[w];
+    const double rstd = 1.0 / __builtin_sqrt(tot / static_cast<double>(p.h_f) +
+                                             static_cast<double>(p.eps));
+    // rstd = m * 2^k; an infinite, zero or NaN rstd (an all-zero row with
+    // eps = 0, an infinite or NaN s) is used as it is, as in the fp32 path.
+    int k = 0;
+    float m = static_cast<float>(rstd);
+    if (rstd > 0.0 && rstd <= 0x1.fffffffffffffp1023) m = static_cast<float>(__builtin_frexp(rstd, &k));
+    float y[VPT][8];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            y[j][e] = (__builtin_ldexpf(acc[j][e], k) * m) * vec_elem(gm[j], e);
+    if (QM != kOutFp8) {
+        const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            u32x4 o;
+            o.x = pack_bf16x2(y[j][0], y[j][1]);
+            o.y = pack_bf16x2(y[j][2], y[j][3]);
+            o.z = pack_bf16x2(y[j][4], y[j][5]);
+            o.w = pack_bf16x2(y[j][6], y[j][7]);
+            buf_store<OUT_AUX>(o, no_r, off[j]);
+        }
+    }
+    if (QM != kOutBf16) {
+        // amax over the row's y (NaN elements aside), then the FP8 rule of
+        // the fp32 path applied to y itself.
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(y[j][e]));
+        const float wm = wave_max(mx);
+        if ((tid & 63) == 0) lds.redm[tid >> 6] = wm;
+        __syncthreads();
+        float amax = 0.0f;
+#pragma unroll 1
+        for (int w = 0; w < nw; ++w) amax = __builtin_fmaxf(amax, lds.redm[w]);
+        const bool zero_row = !(amax > 0.0f);
+        const float qscale = zero_row ? 1.0f : amax / kE4m3Max;
+        // rows whose amax is below 2^-100 are scaled by 2^64 first (exact),
+        // so that 448 / amax cannot overflow
+        const float a = (!zero_row && amax < 0x1p-100f) ? 0x1p64f : 1.0f;
+        const float f = zero_row ? 0.0f : e4m3_factor(amax * a);
+        const rsrc_t q_r = make_rsrc(p.normed_fp8 + t * static_cast<int64_t>(p.V) * 8,
+                                     static_cast<uint32_t>(p.V) * 8u);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (y[j][e] * a) * f;
+            buf_store_b64<OUT_AUX>(pack_e4m3x8(v), q_r, off[j] >> 1);
+        }
+        if (tid == 0) buf_store_b32<kAuxDefault>(qscale, make_rsrc(p.fp8_scale + t, 4u), 0u);
+    }
+}
+
+// The rest of one token once its sum is formed in registers: s = (routed +
+// shared) + residual (the dense tail: x + residual), residual_out, the row
+// reduction behind one barrier (per-wave partials in red, 2 * MAX_WAVES
+// floats of LDS) and the normalised outputs. acc holds the routed part on
+// entry (ignored in the dense tail) and s after.
+template <int VPT, int KT, int OUT_AUX, int QM>
+__device__ __forceinline__ void finish_token(const Params& p, const int64_t t,
+                                             float (&acc)[VPT][8], const u32x4 (&sh)[VPT],
+                                             const u32x4 (&rs)[VPT], const u32x4 (&gm)[VPT],
+                                             const uint32_t (&off)[VPT], float* red, Lds& lds) {
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
     const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
     const int64_t trow = t * static_cast<int64_t>(p.V);
-
-    uint32_t off[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) off[j] = static_cast<uint32_t>(tid + j * nt) * 16u;
-
-    // Order of issue: the routing metadata (scalar loads), then the loads that
-    // do not depend on it (shared, residual, gamma), and only then anything
-    // that waits for the metadata. The scheduling barrier keeps the compiler
-    // from sinking those independent loads below the metadata wait, so every
-    // workgroup starts streaming HBM one memory latency earlier.
     constexpr bool DENSE = KT < 0;
-    constexpr bool CHECK_K = KT != 8;
-    const int32_t* prow = p.perm_idx + t * p.K;
-    const float* wrow = p.topk_w + t * p.K;
-    int32_t idx[8];
-    float wr[8];
-    if constexpr (!DENSE) load_meta8<CHECK_K>(p, prow, wrow, 0, idx, wr);
-
-    const rsrc_t sh_r = make_rsrc(p.shared_out + trow, rowbytes);
-    const rsrc_t rs_r = make_rsrc(p.residual + trow, rowbytes);
-    const rsrc_t gm_r = make_rsrc(p.gamma, rowbytes);
-    u32x4 sh[VPT], rs[VPT], gm[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        sh[j] = buf_load<kAuxActIn>(sh_r, off[j]);
-        rs[j] = buf_load<kAuxActIn>(rs_r, off[j]);
-        gm[j] = buf_load<kAuxGamma>(gm_r, off[j]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    float acc[VPT][8];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
-
-    if constexpr (!DENSE) {
-        bool past_r = gather_rows8<VPT, CHECK_K, ROWS>(p, idx, wr, 0, off, acc);
-        if (CHECK_K && p.K > 8) {
-            load_meta8<true>(p, prow, wrow, 8, idx, wr);
-            past_r |= gather_rows8<VPT, true, ROWS>(p, idx, wr, 8, off, acc);
-        }
-        // Report an index past the rows (its slot was treated as masked).
-        // Every workgroup that sees one writes the same value, so there is
-        // no race on the result.
-        if (ROWS && past_r && p.bad_index != nullptr && tid == 0)
-            buf_store_u32<kAuxDefault>(1u, make_rsrc(p.bad_index, 4u), 0u);
-    }
 
     // s = (routed + shared) + residual (dense: x + residual); per-lane sum of
     // squares, and (FP8 modes) sg = s * gamma with its per-lane max |sg|. s
@@ -276,7 +373,7 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     float rmg = 0.0f;
 #pragma unroll
     for (int w = MAX_WAVES; w < NRED; ++w) rmg = __builtin_fmaxf(rmg, part[w]);
-    const float rstd = rsqrt_f32(tot / p.h_f + p.eps);
+    const float ms_eps = tot / p.h_f + p.eps;
 
     // residual_out = bf16(s), one rounding
     if constexpr (!EARLY_RO) {
@@ -290,6 +387,18 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
             buf_store<OUT_AUX>(o, ro_r, off[j]);
         }
     }
+
+    // Outside the fp32 range of the sum of squares (or, FP8 modes, of
+    // s * gamma), the row is normalised in fp64 instead. NaN lands there too
+    // and stays NaN.
+    bool wide = !(ms_eps >= kRescueBelow && ms_eps <= kFltMax);
+    if (QM != kOutBf16) wide = wide || !(rmg <= kFltMax);
+    if (wide) {
+        normalise_wide<VPT, OUT_AUX, QM>(p, t, acc, off, lds);
+        return;
+    }
+    // ms_eps is a normal number here, which v_rsq_f32 takes as it is
+    const float rstd = __builtin_amdgcn_rsqf(ms_eps);
 
     if (QM != kOutFp8) {
         const rsrc_t no_r = make_rsrc(p.normed_out + trow, rowbytes);
@@ -353,6 +462,71 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
     }
 }
 
+// One token, end to end. KT: 8 = exactly eight slots (the GLM-5.x / DeepSeek
+// top-8 case, no slot-count checks); 0 = any K in 1..16, as one or two
+// chunks of eight; -1 = no routed part (the dense residual add + RMSNorm:
+// shared_out holds x and s = x + residual). Thread i owns the byte offsets 16*(i + j*NT), j < VPT, of
+// every row; offsets at or past the row end (a ragged last tile) fall outside
+// the descriptors' range, so their loads return zero and their stores are
+// dropped by the hardware.
+template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS>
+__device__ __forceinline__ void finalize_token(const Params& p, const int64_t t, Lds& lds) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
+    const int64_t trow = t * static_cast<int64_t>(p.V);
+
+    uint32_t off[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) off[j] = static_cast<uint32_t>(tid + j * nt) * 16u;
+
+    // Order of issue: the routing metadata (scalar loads), then the loads that
+    // do not depend on it (shared, residual, gamma), and only then anything
+    // that waits for the metadata. The scheduling barrier keeps the compiler
+    // from sinking those independent loads below the metadata wait, so every
+    // workgroup starts streaming HBM one memory latency earlier.
+    constexpr bool DENSE = KT < 0;
+    constexpr bool CHECK_K = KT != 8;
+    const int32_t* prow = p.perm_idx + t * p.K;
+    const float* wrow = p.topk_w + t * p.K;
+    int32_t idx[8];
+    float wr[8];
+    if constexpr (!DENSE) load_meta8<CHECK_K>(p, prow, wrow, 0, idx, wr);
+
+    const rsrc_t sh_r = make_rsrc(p.shared_out + trow, rowbytes);
+    const rsrc_t rs_r = make_rsrc(p.residual + trow, rowbytes);
+    const rsrc_t gm_r = make_rsrc(p.gamma, rowbytes);
+    u32x4 sh[VPT], rs[VPT], gm[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        sh[j] = buf_load<kAuxActIn>(sh_r, off[j]);
+        rs[j] = buf_load<kAuxActIn>(rs_r, off[j]);
+        gm[j] = buf_load<kAuxGamma>(gm_r, off[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    float acc[VPT][8];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+
+    if constexpr (!DENSE) {
+        bool past_r = gather_rows8<VPT, CHECK_K, ROWS>(p, idx, wr, 0, off, acc);
+        if (CHECK_K && p.K > 8) {
+            load_meta8<true>(p, prow, wrow, 8, idx, wr);
+            past_r |= gather_rows8<VPT, true, ROWS>(p, idx, wr, 8, off, acc);
+        }
+        // Report an index past the rows (its slot was treated as masked).
+        // Every workgroup that sees one writes the same value, so there is
+        // no race on the result.
+        if (ROWS && past_r && p.bad_index != nullptr && tid == 0)
+            buf_store_u32<kAuxDefault>(1u, make_rsrc(p.bad_index, 4u), 0u);
+    }
+
+    finish_token<VPT, KT, OUT_AUX, QM>(p, t, acc, sh, rs, gm, off, lds.red, lds);
+}
+
 // Launch bound per vectors-per-thread: keeps the register budget large enough
 // that the row vectors in flight never spill.
 template <int VPT>
@@ -374,8 +548,8 @@ __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(
         const int32_t* perm_idx, const float* topk_w, const u32x4* shared_out,
         const u32x4* residual, const u32x4* gamma, const u32x4* expert_out, int V, int K,
         Params p) {
-    // Per-wave row sums and (FP8 modes) row maxima; 16-byte aligned for vector reads.
-    __shared__ __align__(16) float red[2 * MAX_WAVES];
+    // Per-wave partial results of the row reductions; 16-byte aligned for vector reads.
+    __shared__ __align__(16) Lds lds;
     p.perm_idx = perm_idx;
     p.topk_w = topk_w;
     p.shared_out = shared_out;
@@ -384,7 +558,7 @@ __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(
     p.expert_out = expert_out;
     p.V = V;
     p.K = K;
-    finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(p, static_cast<int64_t>(blockIdx.x), red);
+    finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(p, static_cast<int64_t>(blockIdx.x), lds);
 }
 
 }  // namespace mfr
@@ -410,11 +584,17 @@ constexpr int64_t kTokenPathMaxT = 256;
 // the 32 MB of L2 absorbs), write-through from T = 1024 (25 MB) up.
 constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
 
-std::atomic<int> g_force_path{0};
+// The calling thread's launch override (mfr_tuning_force_launch); 0 =
+// automatic. Thread-local, so that one thread's override never changes the
+// launch shape of another thread's call.
+thread_local int t_force_path = 0;
+thread_local int t_force_vpt = 0;
+thread_local int t_force_store = 0;
 
 // Environment switches, read once when the library is loaded:
-//   MFR_PATH=auto|token|stream  default launch path (an override set through
-//                               moe_finalize_rmsnorm_force takes precedence);
+//   MFR_PATH=auto|token|stream  default launch path (a thread's override set
+//                               through mfr_tuning_force_launch takes
+//                               precedence);
 //   MFR_LOG=1                   one line on stderr per launch: shape, path,
 //                               vectors per thread, threads, store policy.
 // An unrecognised MFR_PATH value is reported on stderr and ignored.
@@ -434,8 +614,6 @@ bool env_log() {
 
 const int g_env_path = env_path();
 const bool g_env_log = env_log();
-std::atomic<int> g_force_vpt{0};
-std::atomic<int> g_force_store{0};
 
 int max_threads(int vpt) { return vpt == 1 ? 1024 : 512; }
 
@@ -450,7 +628,7 @@ bool shape_ok(int64_t T, int64_t H, int64_t K) {
 }
 
 int choose_path(int64_t T) {
-    int f = g_force_path.load(std::memory_order_relaxed);
+    int f = t_force_path;
     if (f == 0) f = g_env_path;
     if (f == MFR_PATH_TOKEN || f == MFR_PATH_STREAM) return f;
     return T <= kTokenPathMaxT ? MFR_PATH_TOKEN : MFR_PATH_STREAM;
@@ -460,7 +638,7 @@ int choose_path(int64_t T) {
 // possible (latency); the stream path uses at most 256 threads per token so
 // that more tokens are resident per CU (bandwidth).
 int choose_vpt(int path, int64_t V) {
-    const int f = g_force_vpt.load(std::memory_order_relaxed);
+    const int f = t_force_vpt;
     if (f >= 1 && f <= kVptMax && threads_for(V, f) <= max_threads(f)) return f;
     if (path == MFR_PATH_STREAM) {
         for (int v = 1; v <= kVptMax; ++v)
@@ -472,7 +650,7 @@ int choose_vpt(int path, int64_t V) {
 }
 
 bool write_through(int path, int64_t T, int64_t H) {
-    const int f = g_force_store.load(std::memory_order_relaxed);
+    const int f = t_force_store;
     if (f == MFR_STORE_WRITE_BACK) return false;
     if (f == MFR_STORE_WRITE_THROUGH) return true;
     return path == MFR_PATH_STREAM && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes;
@@ -887,18 +1065,18 @@ const char* moe_finalize_rmsnorm_strerror(int status) {
         case MFR_ERR_ALIAS: return "an output overlaps an input or the other output (only residual_out == residual is allowed)";
         case MFR_ERR_SCALAR: return "eps must be finite and >= 0, scale must be finite";
         case MFR_ERR_HIP: return "the HIP runtime refused the kernel launch";
-        case MFR_ERR_ARG: return "invalid override value";
+        case MFR_ERR_ARG: return "invalid launch override value";
         default: return "unknown status";
     }
 }
 
-int moe_finalize_rmsnorm_force(int path, int vectors_per_thread, int store_policy) {
+int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy) {
     if (path < 0 || path > MFR_PATH_STREAM) return MFR_ERR_ARG;
     if (vectors_per_thread < 0 || vectors_per_thread > kVptMax) return MFR_ERR_ARG;
     if (store_policy < 0 || store_policy > MFR_STORE_WRITE_THROUGH) return MFR_ERR_ARG;
-    g_force_path.store(path, std::memory_order_relaxed);
-    g_force_vpt.store(vectors_per_thread, std::memory_order_relaxed);
-    g_force_store.store(store_policy, std::memory_order_relaxed);
+    t_force_path = path;
+    t_force_vpt = vectors_per_thread;
+    t_force_store = store_policy;
     return MFR_OK;
 }
 

@@ -1,0 +1,44 @@
+/*
+ * mfr_tuning.h - launch override of libmoe_finalize_rmsnorm, for tests,
+ * sweeps and tuning. Not part of the public C ABI
+ * (include/moe_finalize_rmsnorm.h): production callers never need it, and
+ * every entry point picks its launch shape by itself.
+ *
+ * The override belongs to the calling thread: it applies to the later calls
+ * of the entry points (and to moe_finalize_rmsnorm_path) made from that
+ * thread only, so one thread's choice cannot change the launch shape, and
+ * with it the last bit of normed_out, of a call made by another thread.
+ * It takes precedence over the MFR_PATH environment variable.
+ */
+#ifndef MFR_TUNING_H
+#define MFR_TUNING_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mfr_store_policy {
+    MFR_STORE_AUTO = 0,
+    MFR_STORE_WRITE_BACK = 1,
+    MFR_STORE_WRITE_THROUGH = 2
+};
+
+/* path: 0 = automatic, else an mfr_path value (MFR_PATH_TOKEN,
+ * MFR_PATH_STREAM or MFR_PATH_PERSIST; a path that cannot serve a shape
+ * falls back to the automatic one for that call).
+ * vectors_per_thread: 0 = automatic, else 1..4 (16-byte vectors of each row
+ * handled per thread, so the workgroup size follows from H; a value whose
+ * workgroup would exceed the kernel's limit, or that the chosen path does not
+ * take, falls back to automatic).
+ * store_policy: an mfr_store_policy value.
+ * Returns MFR_ERR_ARG (nothing changes) for values outside those ranges,
+ * else MFR_OK. residual_out is bit-identical under every override;
+ * normed_out can differ in the last bit between workgroup shapes, whose
+ * sum-of-squares reduction trees differ. */
+int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFR_TUNING_H */

@@ -16,9 +16,10 @@ Here:
   * ``fused_add_rmsnorm(hidden, residual, gamma, eps)`` is the consumer norm:
     a deferred MoEOutput goes to the fused finalize kernel, a plain tensor
     (attention / dense MLP output) to the dense residual add + RMSNorm kernel;
-  * both kernels are registered as torch custom ops that write into
-    caller-provided outputs, so torch sees their effects and HIP graph capture
-    records them: ``mfr::moe_finalize_rmsnorm`` and ``mfr::residual_add_rmsnorm``
+  * both kernels are registered as torch ops that write into caller-provided
+    outputs, so torch sees their effects (torch.compile traces them) and HIP
+    graph capture records them; an eager call with plain tensors runs the
+    op's kernel directly, without the dispatcher's overhead: ``mfr::moe_finalize_rmsnorm`` and ``mfr::residual_add_rmsnorm``
     write a separate residual_out; ``mfr::moe_finalize_rmsnorm_`` and
     ``mfr::residual_add_rmsnorm_`` update the residual stream in place (it is
     then the one mutated argument, never passed twice); the ``_fp8`` forms of
@@ -35,129 +36,99 @@ from . import binding
 
 _LIB_NS = "mfr"
 
+# The ops are defined on a torch.library.Library with explicit schemas and a
+# plain kernel per device type: dispatch through torch.ops then costs a few
+# microseconds, where torch.library.custom_op's wrapper layers cost several
+# times that per eager call. Each kernel is the binding call itself; the
+# binding refuses tensors off the GPU.
+_LIB = torch.library.Library(_LIB_NS, "DEF")
 
-@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm",
-                         mutates_args=("residual_out", "normed_out"))
-def _moe_finalize_rmsnorm_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
-                             topk_w: torch.Tensor, shared_out: torch.Tensor,
-                             residual: torch.Tensor, gamma: torch.Tensor, eps: float, scale: float,
-                             residual_out: torch.Tensor, normed_out: torch.Tensor) -> None:
+_MOE_ARGS = ("Tensor expert_out, Tensor perm_idx, Tensor topk_w, Tensor shared_out, "
+             "{residual}, Tensor gamma, float eps, float scale")
+_DENSE_ARGS = "Tensor x, {residual}, Tensor gamma, float eps"
+
+
+def _moe_op(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
+            normed_out):
     binding.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
                                  scale, residual_out=residual_out, normed_out=normed_out)
 
 
-@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm",
-                         mutates_args=("residual_out", "normed_out"))
-def _residual_add_rmsnorm_op(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
-                             eps: float, residual_out: torch.Tensor,
-                             normed_out: torch.Tensor) -> None:
-    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual_out,
-                                 normed_out=normed_out)
-
-
-@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm_",
-                         mutates_args=("residual", "normed_out"))
-def _moe_finalize_rmsnorm_inplace_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
-                                     topk_w: torch.Tensor, shared_out: torch.Tensor,
-                                     residual: torch.Tensor, gamma: torch.Tensor, eps: float,
-                                     scale: float, normed_out: torch.Tensor) -> None:
+def _moe_op_(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, normed_out):
     binding.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
                                  scale, residual_out=residual, normed_out=normed_out)
 
 
-@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm_",
-                         mutates_args=("residual", "normed_out"))
-def _residual_add_rmsnorm_inplace_op(x: torch.Tensor, residual: torch.Tensor,
-                                     gamma: torch.Tensor, eps: float,
-                                     normed_out: torch.Tensor) -> None:
-    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual,
-                                 normed_out=normed_out)
-
-
-@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm_fp8",
-                         mutates_args=("residual_out", "normed_fp8", "fp8_scale"))
-def _moe_finalize_rmsnorm_fp8_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
-                                 topk_w: torch.Tensor, shared_out: torch.Tensor,
-                                 residual: torch.Tensor, gamma: torch.Tensor, eps: float,
-                                 scale: float, residual_out: torch.Tensor, normed_fp8: torch.Tensor,
-                                 fp8_scale: torch.Tensor) -> None:
+def _moe_fp8_op(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
+                residual_out, normed_fp8, fp8_scale):
     binding.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
                                      eps, scale, residual_out=residual_out, normed_fp8=normed_fp8,
                                      fp8_scale=fp8_scale)
 
 
-@torch.library.custom_op(f"{_LIB_NS}::moe_finalize_rmsnorm_fp8_",
-                         mutates_args=("residual", "normed_fp8", "fp8_scale"))
-def _moe_finalize_rmsnorm_fp8_inplace_op(expert_out: torch.Tensor, perm_idx: torch.Tensor,
-                                         topk_w: torch.Tensor, shared_out: torch.Tensor,
-                                         residual: torch.Tensor, gamma: torch.Tensor, eps: float,
-                                         scale: float, normed_fp8: torch.Tensor,
-                                         fp8_scale: torch.Tensor) -> None:
+def _moe_fp8_op_(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
+                 normed_fp8, fp8_scale):
     binding.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
                                      eps, scale, residual_out=residual, normed_fp8=normed_fp8,
                                      fp8_scale=fp8_scale)
 
 
-@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm_fp8",
-                         mutates_args=("residual_out", "normed_fp8", "fp8_scale"))
-def _residual_add_rmsnorm_fp8_op(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
-                                 eps: float, residual_out: torch.Tensor, normed_fp8: torch.Tensor,
-                                 fp8_scale: torch.Tensor) -> None:
+def _dense_op(x, residual, gamma, eps, residual_out, normed_out):
+    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual_out,
+                                 normed_out=normed_out)
+
+
+def _dense_op_(x, residual, gamma, eps, normed_out):
+    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual,
+                                 normed_out=normed_out)
+
+
+def _dense_fp8_op(x, residual, gamma, eps, residual_out, normed_fp8, fp8_scale):
     binding.residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=residual_out,
                                      normed_fp8=normed_fp8, fp8_scale=fp8_scale)
 
 
-@torch.library.custom_op(f"{_LIB_NS}::residual_add_rmsnorm_fp8_",
-                         mutates_args=("residual", "normed_fp8", "fp8_scale"))
-def _residual_add_rmsnorm_fp8_inplace_op(x: torch.Tensor, residual: torch.Tensor,
-                                         gamma: torch.Tensor, eps: float,
-                                         normed_fp8: torch.Tensor,
-                                         fp8_scale: torch.Tensor) -> None:
+def _dense_fp8_op_(x, residual, gamma, eps, normed_fp8, fp8_scale):
     binding.residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=residual,
                                      normed_fp8=normed_fp8, fp8_scale=fp8_scale)
 
 
-@_moe_finalize_rmsnorm_fp8_op.register_fake
-def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
-      normed_fp8, fp8_scale):
+def _no_output(*args):
     return None
 
 
-@_moe_finalize_rmsnorm_fp8_inplace_op.register_fake
-def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, normed_fp8,
-      fp8_scale):
-    return None
+# name -> (schema, kernel). Mutated tensors carry alias annotations; the
+# in-place forms (trailing underscore) mutate the residual stream itself.
+_BF16_OUT = "Tensor(b!) normed_out"
+_FP8_OUT = "Tensor(b!) normed_fp8, Tensor(c!) fp8_scale"
+_OPS_DEF = {
+    "moe_finalize_rmsnorm": (
+        _MOE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _BF16_OUT,
+        _moe_op),
+    "moe_finalize_rmsnorm_": (
+        _MOE_ARGS.format(residual="Tensor(a!) residual") + ", " + _BF16_OUT, _moe_op_),
+    "moe_finalize_rmsnorm_fp8": (
+        _MOE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _FP8_OUT,
+        _moe_fp8_op),
+    "moe_finalize_rmsnorm_fp8_": (
+        _MOE_ARGS.format(residual="Tensor(a!) residual") + ", " + _FP8_OUT, _moe_fp8_op_),
+    "residual_add_rmsnorm": (
+        _DENSE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _BF16_OUT,
+        _dense_op),
+    "residual_add_rmsnorm_": (
+        _DENSE_ARGS.format(residual="Tensor(a!) residual") + ", " + _BF16_OUT, _dense_op_),
+    "residual_add_rmsnorm_fp8": (
+        _DENSE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _FP8_OUT,
+        _dense_fp8_op),
+    "residual_add_rmsnorm_fp8_": (
+        _DENSE_ARGS.format(residual="Tensor(a!) residual") + ", " + _FP8_OUT, _dense_fp8_op_),
+}
 
-
-@_residual_add_rmsnorm_fp8_op.register_fake
-def _(x, residual, gamma, eps, residual_out, normed_fp8, fp8_scale):
-    return None
-
-
-@_residual_add_rmsnorm_fp8_inplace_op.register_fake
-def _(x, residual, gamma, eps, normed_fp8, fp8_scale):
-    return None
-
-
-@_moe_finalize_rmsnorm_op.register_fake
-def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
-      normed_out):
-    return None
-
-
-@_residual_add_rmsnorm_op.register_fake
-def _(x, residual, gamma, eps, residual_out, normed_out):
-    return None
-
-
-@_moe_finalize_rmsnorm_inplace_op.register_fake
-def _(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, normed_out):
-    return None
-
-
-@_residual_add_rmsnorm_inplace_op.register_fake
-def _(x, residual, gamma, eps, normed_out):
-    return None
+for _name, (_schema, _kernel) in _OPS_DEF.items():
+    _LIB.define(f"{_name}({_schema}) -> ()")
+    _LIB.impl(_name, _kernel, "CUDA")
+    _LIB.impl(_name, _kernel, "CPU")  # the binding refuses CPU tensors with a clear error
+    torch.library.register_fake(f"{_LIB_NS}::{_name}", _no_output, lib=_LIB)
 
 
 @dataclass
@@ -231,7 +202,7 @@ def _routed(hidden: "MoEOutput"):
     return rows, idx, w, 1.0
 
 
-# (routed part, FP8 output, in place) -> custom op
+# (routed part, FP8 output, in place) -> op name (and its kernel above)
 _OPS = {
     (True, False, False): "moe_finalize_rmsnorm",
     (True, False, True): "moe_finalize_rmsnorm_",
@@ -242,6 +213,17 @@ _OPS = {
     (False, True, False): "residual_add_rmsnorm_fp8",
     (False, True, True): "residual_add_rmsnorm_fp8_",
 }
+_len_dispatch_stack = torch._C._len_torch_dispatch_stack
+
+
+def _direct(ref: torch.Tensor) -> bool:
+    """Whether an eager call may go straight to the op's kernel: a plain
+    tensor, no torch dispatch mode active (fake tensors, functionalization,
+    tracing) and no torch.compile tracing. The kernel is what the dispatcher
+    would run, so results and effects are the same; only the dispatch cost is
+    saved. Anything else goes through torch.ops."""
+    return type(ref) is torch.Tensor and _len_dispatch_stack() == 0 and \
+        not torch.compiler.is_compiling()
 
 
 def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Tensor,
@@ -261,6 +243,8 @@ def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Te
     projection instead: returns (new residual stream, normed_fp8 [T, H]
     float8_e4m3fn, fp8_scale [T] float32), where a token's normed row is
     about normed_fp8 times its scale. normed_fp8 and fp8_scale may be given.
+    A deferred routed part goes through the checked kernel, told the rows of
+    its expert_out, so an out-of-range index is masked rather than read.
     """
     if fp8 and normed_out is not None:
         raise ValueError("fp8=True writes normed_fp8 and fp8_scale, not normed_out")
@@ -283,7 +267,8 @@ def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Te
         args = (rows, idx, w, hidden.shared, residual, gamma, float(eps), scale)
     else:
         args = (hidden, residual, gamma, float(eps))
-    op = getattr(torch.ops.mfr, _OPS[(moe, fp8, r_out is None)])
+    name = _OPS[(moe, fp8, r_out is None)]
+    op = _OPS_DEF[name][1] if _direct(ref) else getattr(torch.ops.mfr, name)
     if r_out is None:
         op(*args, *outs)
         return (residual,) + outs
