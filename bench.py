@@ -742,6 +742,125 @@ def deferred_overhead():
     return out
 
 
+SWEEP_TS = (64, 256, 257, 512, 1024, 2048, 8192)
+
+
+def sweep_shapes(reps=3, cold_bytes=600_000_000):
+    """Every launch shape at the fused op's workload sizes (H = 6144, K = 8):
+    the one-token-per-workgroup kernel at 1..4 vectors per thread (768, 384,
+    256 and 192 threads) with write-back and write-through stores, and the
+    persistent kernel with both store policies, beside the automatic choice.
+    HBM-cold harness: a graph of one call on each of n buffer sets together
+    above cold_bytes (more than twice the Infinity Cache); at T = 8192 one
+    set (1.21 GB) is cold by size. The shapes are timed in turn, in forward
+    then reverse order, reps times; the median per shape is reported. The
+    token and stream paths are automatic choices among these shapes."""
+    import synth
+    from top_finalize_residual_amd import tuning
+    import top_finalize_residual_amd as mfr
+    WB, WT = tuning.STORE_WRITE_BACK, tuning.STORE_WRITE_THROUGH
+    shapes = [(f"v{v}-{'wb' if st == WB else 'wt'}", (mfr.PATH_STREAM, v, st))
+              for v in (1, 2, 3, 4) for st in (WB, WT)]
+    shapes += [("persist-wb", (mfr.PATH_PERSIST, 0, WB)), ("persist-wt", (mfr.PATH_PERSIST, 0, WT)),
+               ("auto", (0, 0, 0))]
+    out = {"H": 6144, "K": 8, "unit": "us", "reps": reps, "T": {}}
+    for T in SWEEP_TS:
+        cfg = "prefill" if T == 8192 else "batch512" if T == 512 else None
+        d = synth.config_inputs(cfg, T) if cfg else synth.generate(
+            T, 6144, 8, scale=2.5, weights="top8_of_256", seed=synth.BASE_SEED + 9000 + T)
+        nb = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+        n = 1 if T == 8192 else max(2, -(-cold_bytes // nb))
+        calls = stacked_calls(d, n, "bf16")
+        per_call = 10 if n == 1 else 1
+        times = {name: [] for name, _ in shapes}
+        for r in range(reps):
+            order = shapes if r % 2 == 0 else shapes[::-1]
+            for name, force in order:
+                scrub_infinity_cache()
+                with tuning.forced(*force):
+                    times[name].append(time_graph(calls, per_call, 3) * 1e3)
+        del calls
+        res = {name: round(sorted(v)[len(v) // 2], 2) for name, v in times.items()}
+        auto_path = mfr.moe_finalize_rmsnorm_path(T, 6144, 8)
+        res["auto_path"] = {1: "token", 2: "stream", 3: "persist"}.get(auto_path, "?")
+        res["bytes"] = nb
+        out["T"][str(T)] = res
+        log(f"sweep T={T}: " + ", ".join(f"{k} {v}" for k, v in res.items() if k != "bytes"))
+    return out
+
+
+def run_sweep(args):
+    import torch
+    torch.cuda.set_device(0)
+    print(json.dumps({"shape_sweep": sweep_shapes(reps=args.sweep_reps)}), flush=True)
+
+
+# Input states of the bandwidth figures: (name, T, buffer sets cycled, calls
+# per set and graph); see input_states().
+STATE_PHASES = (
+    ("prefill_T8192_1set", 8192, 1, 8),
+    ("prefill_T8192_2sets", 8192, 2, 4),
+    ("prefill_T8192_4sets", 8192, 4, 2),
+    ("batch_T512_8sets_graph64", 512, 8, 8),
+    ("batch_T512_32sets_graph64", 512, 32, 2),
+    ("batch_T512_8sets_graph8", 512, 8, 1),
+)
+
+
+def _state_sets(cache, T, n):
+    """n device copies of the workload at T (shared between phases)."""
+    import synth
+    cfg = "prefill" if T == 8192 else "batch512"
+    key = (T, n)
+    if key not in cache:
+        cache[key] = stacked_calls(synth.config_inputs(cfg, T), n, "bf16")
+    return cache[key]
+
+
+def input_states(reps=3, eager=False, log_phase=None):
+    """The fused op at T = 8192 and 512 in the input states its bandwidth
+    depends on: one buffer set re-read call after call, or several distinct
+    sets cycled (1, 2 and 4 sets of 1.41 GB at T = 8192; 8 and 32 sets of
+    75.5 MB at T = 512). Each phase times graphs of n_sets x per_set calls
+    (median of reps), or, with eager, plain launches in the same order (for
+    a counter run, whose dispatches then map to phases by position)."""
+    import synth
+    cache = {}
+    out = {}
+    for name, T, n, per_set in STATE_PHASES:
+        calls = _state_sets(cache, T, n)
+        nb = synth.config_algorithmic_bytes("prefill" if T == 8192 else "batch512", T)
+        if eager:
+            for _ in range(per_set):
+                for c in calls:
+                    c()
+            import torch
+            torch.cuda.synchronize()
+            if log_phase:
+                log_phase(name, per_set * n)
+            continue
+        scrub_infinity_cache()
+        ts = sorted(time_graph(calls, per_set, 3) * 1e3 for _ in range(reps))
+        us = ts[len(ts) // 2]
+        out[name] = {"us": round(us, 2), "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "sets": n, "footprint_gb": round(n * nb / 1e9, 2),
+                     "calls_per_graph": n * per_set}
+        if T == 8192 and n == 4:
+            del cache[(T, 1)], cache[(T, 2)]  # keep the device footprint bounded
+    return out
+
+
+def run_states(args):
+    """Eager launches of every input-state phase, in order, for a counter
+    run; prints the phase table (name, dispatches) as JSON."""
+    import torch
+    torch.cuda.set_device(0)
+    phases = []
+    input_states(eager=True, log_phase=lambda name, n: phases.append({"phase": name,
+                                                                         "dispatches": n}))
+    print(json.dumps({"state_phases": phases}), flush=True)
+
+
 def run_latency(args):
     """Eager calls for a kernel trace, small sizes first so that no large call
     has flushed the caches before them: the fused op at the decode sizes, the
@@ -1113,6 +1232,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip copy ceiling, decode sweep, 512 batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="time every launch shape at T = 64..8192 (H=6144, K=8), HBM-cold")
+    ap.add_argument("--sweep-reps", type=int, default=3)
+    ap.add_argument("--state-run", action="store_true",
+                    help="eager launches of the input-state phases, for a counter run")
     ap.add_argument("--latency-run", action="store_true")
     ap.add_argument("--summarize-trace")
     ap.add_argument("--kernel-filter", default="mfr_")
@@ -1150,6 +1274,10 @@ def main():
         return run_pmc_variants(args)
     if args.latency_run:
         return run_latency(args)
+    if args.shape_sweep:
+        return run_sweep(args)
+    if args.state_run:
+        return run_states(args)
     return run_bench(args)
 
 

@@ -107,13 +107,19 @@ enum mfr_status {
     MFR_ERR_ARG = 7     /* an invalid launch override (the library's tuning interface) */
 };
 
-/* Both paths launch one workgroup per token (grid = T); they differ in launch
- * shape and store policy. */
+/* Launch paths. The token and stream paths launch one workgroup per token
+ * (grid = T) and differ in workgroup shape and store policy; the persistent
+ * path launches a grid sized to the GPU, each workgroup walking many tokens
+ * with the next token's loads in flight while it finishes the current one.
+ * All give bit-identical residual_out; normed_out can differ in the last bit
+ * between workgroup shapes (their reduction trees differ). */
 enum mfr_path {
     MFR_PATH_UNSUPPORTED = 0,
-    MFR_PATH_TOKEN = 1,  /* small T, latency: widest workgroup per token (768 threads at H = 6144) */
-    MFR_PATH_STREAM = 2  /* large T, bandwidth: 256 threads per token, write-through stores once
-                            the outputs outgrow the L2 */
+    MFR_PATH_TOKEN = 1,   /* small T, latency: widest workgroup per token (768 threads at H = 6144) */
+    MFR_PATH_STREAM = 2,  /* large T, bandwidth: 256 threads per token, write-through stores once
+                             the outputs outgrow the L2 */
+    MFR_PATH_PERSIST = 3  /* large T, bandwidth: persistent multi-token workgroups, two tokens in
+                             flight each (H <= 6144, K <= 8) */
 };
 
 /* The fused op. Definition, layouts, limits and errors: see above. */

@@ -11,6 +11,7 @@ hand-written HIP kernels for gfx950 behind a C ABI
 """
 from .binding import (  # noqa: F401
     MFRError,
+    PATH_PERSIST,
     PATH_STREAM,
     PATH_TOKEN,
     PATH_UNSUPPORTED,

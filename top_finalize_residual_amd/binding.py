@@ -36,6 +36,7 @@ MFR_ERR_ARG = 7
 PATH_UNSUPPORTED = 0
 PATH_TOKEN = 1
 PATH_STREAM = 2
+PATH_PERSIST = 3
 
 LIB_PATH = _build.LIB
 if not os.path.exists(LIB_PATH):

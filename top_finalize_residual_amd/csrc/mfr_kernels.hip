@@ -45,6 +45,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -561,6 +562,133 @@ __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(
     finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(p, static_cast<int64_t>(blockIdx.x), lds);
 }
 
+
+// ---------------------------------------------------------------------------
+// Persistent multi-token path (large T): a grid sized to the GPU's resident
+// capacity, each workgroup walking the tokens blockIdx.x, blockIdx.x + G,
+// blockIdx.x + 2G, ... (G = gridDim.x), one 16-byte vector per thread per row.
+// Software-pipelined over two register buffers: the next token's K row loads
+// and its shared and residual loads are issued before the current token is
+// reduced, normalised and stored, so each workgroup keeps a token's reads in
+// flight while it finishes the previous one (the page's fix gathers the
+// routes of a token together; here the gather of the next token also
+// overlaps the tail of the current one: vLLM pull request #62174,
+// Validation). The two buffers keep fixed roles in a loop unrolled by two, so
+// no register holding a load in flight is ever copied. A step past the last
+// token issues its loads through zero-record descriptors (no memory access),
+// so every path through the loop issues the same instructions and the load
+// counters stay exact. The reduction slots in LDS alternate between two sets
+// by token parity: one barrier per token then suffices, because a wave
+// writes a slot set again only after every wave has passed the next barrier,
+// and so has read it.
+// ---------------------------------------------------------------------------
+
+// At most 768 threads (12 waves, 3 per SIMD), so that the two register
+// buffers fit in the 168 VGPRs a wave may then hold: H up to 6144.
+constexpr int kPersistMaxThreads = 768;
+
+struct LdsPersist {
+    Lds lds;                     // even tokens' slots (lds.red), the range-rescue slots
+    float red_b[2 * MAX_WAVES];  // odd tokens' slots
+};
+
+// Issues every load of token t that depends on no reduction: shared and
+// residual rows, then (routed kernels) the K <= 8 gathered rows, all in
+// flight on return. live = false loads nothing (zero-record descriptors; t
+// is then any valid token, only used to form addresses).
+template <int KT, bool ROWS>
+__device__ __forceinline__ bool issue_token(const Params& p, const int64_t t, const bool live,
+                                            const int32_t (&idx)[8], const float (&wr)[8],
+                                            const uint32_t (&off)[1], u32x4 (&r)[8][1],
+                                            float (&w)[8], u32x4 (&sh)[1], u32x4 (&rs)[1]) {
+    const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
+    const int64_t trow = t * static_cast<int64_t>(p.V);
+    sh[0] = buf_load<kAuxActIn>(make_rsrc(p.shared_out + trow, live ? rowbytes : 0u), off[0]);
+    rs[0] = buf_load<kAuxActIn>(make_rsrc(p.residual + trow, live ? rowbytes : 0u), off[0]);
+    if constexpr (KT >= 0)
+        return issue_rows8<1, KT != 8, ROWS>(p, idx, wr, 0, off, r, w, live);
+    return false;
+}
+
+// The routing metadata of token t (clamped to the last token: a step past
+// the end reads a valid row of perm_idx and topk_w and uses none of it).
+template <int KT>
+__device__ __forceinline__ void persist_meta(const Params& p, int64_t t, int32_t (&idx)[8],
+                                             float (&wr)[8]) {
+    if constexpr (KT >= 0) {
+        if (t >= p.T) t = p.T - 1;
+        load_meta8<KT != 8>(p, p.perm_idx + t * p.K, p.topk_w + t * p.K, 0, idx, wr);
+    }
+}
+
+template <int KT, int OUT_AUX, int QM>
+__device__ __forceinline__ void persist_finish(const Params& p, const int64_t t,
+                                               const u32x4 (&r)[8][1], const float (&w)[8],
+                                               const u32x4 (&sh)[1], const u32x4 (&rs)[1],
+                                               const u32x4 (&gm)[1], const uint32_t (&off)[1],
+                                               float* red, Lds& lds) {
+    float acc[1][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[0][e] = 0.0f;
+    if constexpr (KT >= 0) fold_rows8<1>(r, w, acc);
+    finish_token<1, KT, OUT_AUX, QM>(p, t, acc, sh, rs, gm, off, red, lds);
+}
+
+// KT: 8 or 0 (any K <= 8: the host routes K > 8 elsewhere) or -1 (dense).
+// The grid is at most T workgroups, so every workgroup's first token exists.
+template <int KT, int OUT_AUX, int QM, bool ROWS = false>
+__global__ __launch_bounds__(kPersistMaxThreads) void mfr_persist_kernel(
+        const int32_t* perm_idx, const float* topk_w, const u32x4* shared_out,
+        const u32x4* residual, const u32x4* gamma, const u32x4* expert_out, int V, int K,
+        Params p) {
+    __shared__ __align__(16) LdsPersist L;
+    p.perm_idx = perm_idx;
+    p.topk_w = topk_w;
+    p.shared_out = shared_out;
+    p.residual = residual;
+    p.gamma = gamma;
+    p.expert_out = expert_out;
+    p.V = V;
+    p.K = K;
+    const uint32_t off[1] = {static_cast<uint32_t>(threadIdx.x) * 16u};
+    const int64_t G = gridDim.x;
+    int64_t t = blockIdx.x;
+
+    int32_t idx[8];
+    float wr[8];
+    u32x4 ra[8][1], rb[8][1], sha[1], rsa[1], shb[1], rsb[1];
+    float wa[8], wb[8];
+    bool past_r = false;
+    // gamma: one row for every token, loaded once
+    const u32x4 gm[1] = {buf_load<kAuxGamma>(make_rsrc(p.gamma, static_cast<uint32_t>(V) * 16u),
+                                             off[0])};
+    persist_meta<KT>(p, t, idx, wr);
+    past_r |= issue_token<KT, ROWS>(p, t, true, idx, wr, off, ra, wa, sha, rsa);
+    persist_meta<KT>(p, t + G, idx, wr);
+    for (;;) {
+        // buffer B <- token t + G; finish token t from buffer A
+        const int64_t tb = t + G;
+        const bool lb = tb < p.T;
+        past_r |= issue_token<KT, ROWS>(p, lb ? tb : t, lb, idx, wr, off, rb, wb, shb, rsb);
+        persist_meta<KT>(p, tb + G, idx, wr);
+        persist_finish<KT, OUT_AUX, QM>(p, t, ra, wa, sha, rsa, gm, off, L.lds.red, L.lds);
+        if (!lb) break;
+        t = tb;
+        // buffer A <- token t + G; finish token t from buffer B
+        const int64_t ta = t + G;
+        const bool la = ta < p.T;
+        past_r |= issue_token<KT, ROWS>(p, la ? ta : t, la, idx, wr, off, ra, wa, sha, rsa);
+        persist_meta<KT>(p, ta + G, idx, wr);
+        persist_finish<KT, OUT_AUX, QM>(p, t, rb, wb, shb, rsb, gm, off, L.red_b, L.lds);
+        if (!la) break;
+        t = ta;
+    }
+    // An index past the rows was treated as masked; report it (every
+    // workgroup that saw one writes the same value).
+    if (ROWS && past_r && p.bad_index != nullptr && threadIdx.x == 0)
+        buf_store_u32<kAuxDefault>(1u, make_rsrc(p.bad_index, 4u), 0u);
+}
+
 }  // namespace mfr
 
 // ---------------------------------------------------------------------------
@@ -590,11 +718,12 @@ constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
 thread_local int t_force_path = 0;
 thread_local int t_force_vpt = 0;
 thread_local int t_force_store = 0;
+thread_local int t_force_residency = 0;  // persistent path: workgroups per CU (0 = all that fit)
 
 // Environment switches, read once when the library is loaded:
-//   MFR_PATH=auto|token|stream  default launch path (a thread's override set
-//                               through mfr_tuning_force_launch takes
-//                               precedence);
+//   MFR_PATH=auto|token|stream|persist  default launch path (a thread's
+//                               override set through mfr_tuning_force_launch
+//                               takes precedence);
 //   MFR_LOG=1                   one line on stderr per launch: shape, path,
 //                               vectors per thread, threads, store policy.
 // An unrecognised MFR_PATH value is reported on stderr and ignored.
@@ -603,7 +732,9 @@ int env_path() {
     if (!v || !*v || std::strcmp(v, "auto") == 0) return 0;
     if (std::strcmp(v, "token") == 0) return MFR_PATH_TOKEN;
     if (std::strcmp(v, "stream") == 0) return MFR_PATH_STREAM;
-    std::fprintf(stderr, "moe_finalize_rmsnorm: ignoring MFR_PATH=%s (auto, token or stream)\n", v);
+    if (std::strcmp(v, "persist") == 0) return MFR_PATH_PERSIST;
+    std::fprintf(stderr,
+                 "moe_finalize_rmsnorm: ignoring MFR_PATH=%s (auto, token, stream or persist)\n", v);
     return 0;
 }
 
@@ -627,10 +758,21 @@ bool shape_ok(int64_t T, int64_t H, int64_t K) {
     return T >= 0 && T <= kTMax && H >= 8 && H <= kHMax && H % 8 == 0 && K >= 1 && K <= kKMax;
 }
 
-int choose_path(int64_t T) {
+// The persistent path keeps one 16-byte vector per thread per row and at
+// most eight gathered rows in each of its two register buffers: H up to 6144
+// (768 threads) and K up to 8 (any K for the dense tail, which gathers
+// nothing).
+bool persist_ok(int64_t H, int64_t K) {
+    return threads_for(H / 8, 1) <= mfr::kPersistMaxThreads && K <= 8;
+}
+
+// Launch path of a shape (K = 1 for the dense tail). A forced path that
+// cannot serve the shape falls back to the automatic choice.
+int choose_path(int64_t T, int64_t H, int64_t K) {
     int f = t_force_path;
     if (f == 0) f = g_env_path;
-    if (f == MFR_PATH_TOKEN || f == MFR_PATH_STREAM) return f;
+    if (f == MFR_PATH_PERSIST && !persist_ok(H, K)) f = 0;
+    if (f == MFR_PATH_TOKEN || f == MFR_PATH_STREAM || f == MFR_PATH_PERSIST) return f;
     return T <= kTokenPathMaxT ? MFR_PATH_TOKEN : MFR_PATH_STREAM;
 }
 
@@ -653,7 +795,7 @@ bool write_through(int path, int64_t T, int64_t H) {
     const int f = t_force_store;
     if (f == MFR_STORE_WRITE_BACK) return false;
     if (f == MFR_STORE_WRITE_THROUGH) return true;
-    return path == MFR_PATH_STREAM && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes;
+    return path != MFR_PATH_TOKEN && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes;
 }
 
 bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
@@ -704,6 +846,74 @@ const void* kernel_for(int vpt, Variant v, bool wt, int qm) {
         case 3: return pick<3>(v, wt, qm);
         default: return pick<4>(v, wt, qm);
     }
+}
+
+template <int KT, int QM, bool ROWS = false>
+const void* pick_persist_store(bool wt) {
+    return wt ? reinterpret_cast<const void*>(
+                    &mfr::mfr_persist_kernel<KT, mfr::kAuxWriteThrough, QM, ROWS>)
+              : reinterpret_cast<const void*>(&mfr::mfr_persist_kernel<KT, mfr::kAuxOut, QM, ROWS>);
+}
+
+template <int QM>
+const void* pick_persist_variant(Variant v, bool wt) {
+    switch (v) {
+        case kTop8: return pick_persist_store<8, QM>(wt);
+        case kAnyK: return pick_persist_store<0, QM>(wt);
+        case kTop8Rows: return pick_persist_store<8, QM, true>(wt);
+        case kAnyKRows: return pick_persist_store<0, QM, true>(wt);
+        default: return pick_persist_store<-1, QM>(wt);
+    }
+}
+
+// Persistent kernel for (routing variant, write-through outputs, output mode).
+const void* persist_kernel_for(Variant v, bool wt, int qm) {
+    switch (qm) {
+        case mfr::kOutFp8: return pick_persist_variant<mfr::kOutFp8>(v, wt);
+        case mfr::kOutBoth: return pick_persist_variant<mfr::kOutBoth>(v, wt);
+        default: return pick_persist_variant<mfr::kOutBf16>(v, wt);
+    }
+}
+
+// Compute units of the calling thread's current device, queried once per
+// device (the only state the library keeps besides the per-kernel residency
+// below; both are filled on first use and never change).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>* slot = dev < kMaxDevices ? &g_cus[dev] : nullptr;
+    int n = slot ? slot->load(std::memory_order_relaxed) : 0;
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return 1;
+    if (slot) slot->store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of nt threads of one kernel that fit on a CU at once (from the
+// kernel's register and LDS use), queried once per (kernel, nt).
+struct Residency {
+    const void* kern;
+    int nt;
+    int per_cu;
+};
+std::mutex g_res_mu;
+Residency g_res[512];
+int g_res_n = 0;
+
+int resident_per_cu(const void* kern, int nt) {
+    std::lock_guard<std::mutex> lock(g_res_mu);
+    for (int i = 0; i < g_res_n; ++i)
+        if (g_res[i].kern == kern && g_res[i].nt == nt) return g_res[i].per_cu;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, nt, 0) != hipSuccess || n <= 0)
+        return 1;
+    if (g_res_n < 512) g_res[g_res_n++] = {kern, nt, n};
+    return n;
 }
 
 // Aliasing rule shared by the entry points: no output may overlap another
@@ -763,10 +973,34 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     p.T = T;
     p.h_f = static_cast<float>(H);
     p.V = static_cast<int>(H / 8);
-    const int path = choose_path(T);
+    const int path = choose_path(T, H, v == kDense ? 1 : p.K);
+    const bool wt = write_through(path, T, H);
+    if (path == MFR_PATH_PERSIST) {
+        // one launch, a grid of at most T workgroups sized to what the GPU
+        // holds at once; each workgroup walks its tokens
+        const int nt = threads_for(p.V, 1);
+        const void* kern = persist_kernel_for(v, wt, qm);
+        int per_cu = resident_per_cu(kern, nt);
+        if (t_force_residency > 0 && t_force_residency < per_cu) per_cu = t_force_residency;
+        const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu;
+        const int64_t grid = T < cap ? T : cap;
+        if (g_env_log)
+            std::fprintf(stderr,
+                         "moe_finalize_rmsnorm: T=%lld H=%lld K=%d variant=%s out=%s path=persist "
+                         "vpt=1 threads=%d stores=%s workgroups=%lld\n",
+                         static_cast<long long>(T), static_cast<long long>(H), p.K,
+                         v == kTop8 ? "top8" : v == kAnyK ? "anyK" : v == kTop8Rows ? "top8-rows" :
+                         v == kAnyKRows ? "anyK-rows" : "dense",
+                         qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16", nt,
+                         wt ? "write-through" : "write-back", static_cast<long long>(grid));
+        void* args[] = {&p.perm_idx, &p.topk_w, &p.shared_out, &p.residual, &p.gamma,
+                        &p.expert_out, &p.V, &p.K, &p};
+        const hipError_t e =
+            hipLaunchKernel(kern, dim3(static_cast<uint32_t>(grid)), dim3(nt), args, 0, stream);
+        return e == hipSuccess ? MFR_OK : MFR_ERR_HIP;
+    }
     const int vpt = choose_vpt(path, p.V);
     const int nt = threads_for(p.V, vpt);
-    const bool wt = write_through(path, T, H);
     const void* kern = kernel_for(vpt, v, wt, qm);
     const int64_t per = tokens_per_dispatch(nt);
     if (g_env_log)
@@ -1051,7 +1285,7 @@ int residual_add_rmsnorm_fp8(const uint16_t* x, const uint16_t* residual, const 
 
 int moe_finalize_rmsnorm_path(int64_t T, int64_t H, int64_t K) {
     if (!shape_ok(T, H, K)) return MFR_PATH_UNSUPPORTED;
-    return choose_path(T == 0 ? 1 : T);
+    return choose_path(T == 0 ? 1 : T, H, K);
 }
 
 const char* moe_finalize_rmsnorm_strerror(int status) {
@@ -1071,12 +1305,18 @@ const char* moe_finalize_rmsnorm_strerror(int status) {
 }
 
 int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy) {
-    if (path < 0 || path > MFR_PATH_STREAM) return MFR_ERR_ARG;
+    if (path < 0 || path > MFR_PATH_PERSIST) return MFR_ERR_ARG;
     if (vectors_per_thread < 0 || vectors_per_thread > kVptMax) return MFR_ERR_ARG;
     if (store_policy < 0 || store_policy > MFR_STORE_WRITE_THROUGH) return MFR_ERR_ARG;
     t_force_path = path;
     t_force_vpt = vectors_per_thread;
     t_force_store = store_policy;
+    return MFR_OK;
+}
+
+int mfr_tuning_force_residency(int workgroups_per_cu) {
+    if (workgroups_per_cu < 0) return MFR_ERR_ARG;
+    t_force_residency = workgroups_per_cu;
     return MFR_OK;
 }
 

@@ -37,6 +37,12 @@ enum mfr_store_policy {
  * sum-of-squares reduction trees differ. */
 int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy);
 
+/* Workgroups per CU of the persistent path's grid, for the calling thread:
+ * 0 = as many as fit at once (the default), else at most that many. The grid
+ * is that times the CU count, and never more than T. Returns MFR_ERR_ARG for
+ * a negative value, else MFR_OK. */
+int mfr_tuning_force_residency(int workgroups_per_cu);
+
 #ifdef __cplusplus
 }
 #endif
