@@ -745,7 +745,7 @@ def deferred_overhead():
 SWEEP_TS = (64, 256, 257, 512, 1024, 2048, 8192)
 
 
-def sweep_shapes(reps=3, cold_bytes=600_000_000):
+def sweep_shapes(reps=3, cold_bytes=600_000_000, phases=None, ts=SWEEP_TS):
     """Every launch shape at the fused op's workload sizes (H = 6144, K = 8):
     the one-token-per-workgroup kernel at 1..4 vectors per thread (768, 384,
     256 and 192 threads) with write-back and write-through stores, and the
@@ -754,7 +754,13 @@ def sweep_shapes(reps=3, cold_bytes=600_000_000):
     above cold_bytes (more than twice the Infinity Cache); at T = 8192 one
     set (1.21 GB) is cold by size. The shapes are timed in turn, in forward
     then reverse order, reps times; the median per shape is reported. The
-    token and stream paths are automatic choices among these shapes."""
+    token and stream paths are automatic choices among these shapes.
+
+    With phases (a list), the calls are launched eagerly instead, in the same
+    order, and each (T, shape) group is appended to phases as
+    {label, dispatches, bytes}, so that a kernel trace of the run maps its
+    dispatches to shapes by position."""
+    import torch
     import synth
     from top_finalize_residual_amd import tuning
     import top_finalize_residual_amd as mfr
@@ -764,7 +770,7 @@ def sweep_shapes(reps=3, cold_bytes=600_000_000):
     shapes += [("persist-wb", (mfr.PATH_PERSIST, 0, WB)), ("persist-wt", (mfr.PATH_PERSIST, 0, WT)),
                ("auto", (0, 0, 0))]
     out = {"H": 6144, "K": 8, "unit": "us", "reps": reps, "T": {}}
-    for T in SWEEP_TS:
+    for T in ts:
         cfg = "prefill" if T == 8192 else "batch512" if T == 512 else None
         d = synth.config_inputs(cfg, T) if cfg else synth.generate(
             T, 6144, 8, scale=2.5, weights="top8_of_256", seed=synth.BASE_SEED + 9000 + T)
@@ -778,8 +784,18 @@ def sweep_shapes(reps=3, cold_bytes=600_000_000):
             for name, force in order:
                 scrub_infinity_cache()
                 with tuning.forced(*force):
-                    times[name].append(time_graph(calls, per_call, 3) * 1e3)
+                    if phases is None:
+                        times[name].append(time_graph(calls, per_call, 3) * 1e3)
+                        continue
+                    for _ in range(per_call):
+                        for c in calls:
+                            c()
+                    torch.cuda.synchronize()
+                    phases.append({"label": f"T{T}/{name}", "dispatches": per_call * len(calls),
+                                   "bytes": nb})
         del calls
+        if phases is not None:
+            continue
         res = {name: round(sorted(v)[len(v) // 2], 2) for name, v in times.items()}
         auto_path = mfr.moe_finalize_rmsnorm_path(T, 6144, 8)
         res["auto_path"] = {1: "token", 2: "stream", 3: "persist"}.get(auto_path, "?")
@@ -792,7 +808,13 @@ def sweep_shapes(reps=3, cold_bytes=600_000_000):
 def run_sweep(args):
     import torch
     torch.cuda.set_device(0)
-    print(json.dumps({"shape_sweep": sweep_shapes(reps=args.sweep_reps)}), flush=True)
+    ts = tuple(int(x) for x in args.sweep_ts.split(",")) if args.sweep_ts else SWEEP_TS
+    if args.eager:
+        phases = []
+        sweep_shapes(reps=args.sweep_reps, phases=phases, ts=ts)
+        print(json.dumps({"phases": phases}), flush=True)
+        return
+    print(json.dumps({"shape_sweep": sweep_shapes(reps=args.sweep_reps, ts=ts)}), flush=True)
 
 
 # Input states of the bandwidth figures: (name, T, buffer sets cycled, calls
@@ -807,17 +829,19 @@ STATE_PHASES = (
 )
 
 
-def _state_sets(cache, T, n):
+def _state_sets(cache, T, n, inputs):
     """n device copies of the workload at T (shared between phases)."""
     import synth
     cfg = "prefill" if T == 8192 else "batch512"
     key = (T, n)
     if key not in cache:
-        cache[key] = stacked_calls(synth.config_inputs(cfg, T), n, "bf16")
+        if T not in inputs:
+            inputs[T] = synth.config_inputs(cfg, T)
+        cache[key] = stacked_calls(inputs[T], n, "bf16")
     return cache[key]
 
 
-def input_states(reps=3, eager=False, log_phase=None):
+def input_states(reps=3, eager=False, log_phase=None, prefill=None):
     """The fused op at T = 8192 and 512 in the input states its bandwidth
     depends on: one buffer set re-read call after call, or several distinct
     sets cycled (1, 2 and 4 sets of 1.41 GB at T = 8192; 8 and 32 sets of
@@ -826,9 +850,10 @@ def input_states(reps=3, eager=False, log_phase=None):
     a counter run, whose dispatches then map to phases by position)."""
     import synth
     cache = {}
+    inputs = {} if prefill is None else {8192: prefill}
     out = {}
     for name, T, n, per_set in STATE_PHASES:
-        calls = _state_sets(cache, T, n)
+        calls = _state_sets(cache, T, n, inputs)
         nb = synth.config_algorithmic_bytes("prefill" if T == 8192 else "batch512", T)
         if eager:
             for _ in range(per_set):
@@ -855,10 +880,43 @@ def run_states(args):
     run; prints the phase table (name, dispatches) as JSON."""
     import torch
     torch.cuda.set_device(0)
+    import synth
     phases = []
-    input_states(eager=True, log_phase=lambda name, n: phases.append({"phase": name,
-                                                                         "dispatches": n}))
-    print(json.dumps({"state_phases": phases}), flush=True)
+
+    def add(name, n):
+        T = 8192 if "T8192" in name else 512
+        nb = synth.config_algorithmic_bytes("prefill" if T == 8192 else "batch512", T)
+        phases.append({"label": name, "dispatches": n, "bytes": nb})
+    input_states(eager=True, log_phase=add)
+    print(json.dumps({"phases": phases}), flush=True)
+
+
+def run_persist_counters(args):
+    """For a counter run: the automatic (grid of tokens) and the persistent
+    launch of the fused op at T = 512, 2048 and 8192 (H = 6144, K = 8), a few
+    calls each on one buffer set, then one 1 GiB copy of known size for the
+    counters' calibration; prints the phase table."""
+    import torch
+    import synth
+    import top_finalize_residual_amd as mfr
+    from top_finalize_residual_amd import tuning
+    torch.cuda.set_device(0)
+    phases = []
+    for T in (512, 2048, 8192):
+        cfg = "prefill" if T == 8192 else "batch512" if T == 512 else None
+        d = synth.config_inputs(cfg, T) if cfg else synth.generate(
+            T, 6144, 8, scale=2.5, weights="top8_of_256", seed=synth.BASE_SEED + 9000 + T)
+        nb = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+        call = stacked_calls(d, 1, "bf16")[0]
+        for name, path in (("auto", 0), ("persist", mfr.PATH_PERSIST)):
+            with tuning.forced(path):
+                for _ in range(args.steps):
+                    call()
+            torch.cuda.synchronize()
+            phases.append({"label": f"T{T}/{name}", "dispatches": args.steps, "bytes": nb})
+        del call
+    probe_ceilings(reps=1)
+    print(json.dumps({"phases": phases}), flush=True)
 
 
 def run_latency(args):
@@ -955,6 +1013,8 @@ def run_bench(args):
         rec["row_layouts"] = layout_figures(d)
         log("deferred-finalize torch path: host overhead")
         rec["deferred_path"] = deferred_overhead()
+        log("input states: one buffer set re-read, or several cycled (T = 8192 and 512)")
+        rec["input_states"] = input_states(prefill=d)
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on the same workload (single thread)")
         rec["cpu_baseline"] = cpu_baseline(d)
@@ -1035,6 +1095,140 @@ def summarize_trace(args):
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+FUSED_KERNELS = ("mfr_fused_kernel", "mfr_persist_kernel")
+
+
+def _dispatch_rows(path):
+    """Rows of a rocprofv3 kernel_trace.csv or counter_collection.csv, in
+    dispatch order."""
+    rows = list(csv.DictReader(open(path)))
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Correlation_Id"
+    if rows and key in rows[0]:
+        rows.sort(key=lambda r: int(r[key]))
+    return rows
+
+
+def summarize_phases(args):
+    """Durations (from a kernel trace) or counters (from counter runs) of the
+    fused kernels of a phase run, attributed to its phases by dispatch order:
+    the n-th fused-kernel dispatch of the run belongs to the phase whose
+    dispatch range holds n. Counter files give one value per dispatch and
+    counter; FETCH_SIZE and WRITE_SIZE are also calibrated on the 1 GiB copy
+    probe of the same run when present, as traffic against each phase's
+    algorithmic bytes."""
+    import statistics
+    with open(args.phases_json) as f:
+        phases = None
+        for ln in f:
+            ln = ln.strip()
+            if ln.startswith("{") and '"phases"' in ln:
+                phases = json.loads(ln)["phases"]
+    if phases is None:
+        raise SystemExit(f"no phase table in {args.phases_json}")
+    bounds, n = [], 0
+    for ph in phases:
+        bounds.append((n, n + ph["dispatches"], ph["label"]))
+        n += ph["dispatches"]
+    label_of = {}
+    for a, b, label in bounds:
+        for i in range(a, b):
+            label_of[i] = label
+    order = list(dict.fromkeys(ph["label"] for ph in phases))
+    nbytes = {ph["label"]: ph.get("bytes") for ph in phases}
+    lines = [f"# {args.title}", "", "Commands ($REPO is the repository root, $OUT any output "
+             "directory):", "", "```", args.command, "```", ""]
+    if args.trace_csv:
+        rows = [r for r in _dispatch_rows(args.trace_csv)
+                if any(k in r["Kernel_Name"] for k in FUSED_KERNELS)]
+        if len(rows) != n:
+            raise SystemExit(f"{len(rows)} fused-kernel dispatches in the trace, {n} in the phases")
+        per = {}
+        names = {}
+        for i, r in enumerate(rows):
+            lab = label_of[i]
+            per.setdefault(lab, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            names.setdefault(lab, set()).add((r["Kernel_Name"].split("(")[0].replace("void ", ""),
+                                              int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])))
+        lines += ["| phase | kernel (grid threads / workgroup) | dispatches | avg µs | median µs | "
+                  "min µs | max µs | GB/s (median) |", "|---|---|---|---|---|---|---|---|"]
+        for lab in order:
+            v = per[lab]
+            med = statistics.median(v)
+            kn = "; ".join(f"`{k}` ({g}/{w})" for k, g, w in sorted(names[lab]))
+            gbs = f"{nbytes[lab] / (med * 1e-6) / 1e9:,.0f}" if nbytes.get(lab) else ""
+            lines.append(f"| {lab} | {kn} | {len(v)} | {statistics.mean(v):.2f} | {med:.2f} | "
+                         f"{min(v):.2f} | {max(v):.2f} | {gbs} |")
+    else:
+        vals = {}  # (label, counter) -> values
+        copy = {}
+        for path in args.counter_csv:
+            rows = _dispatch_rows(path)
+            counters = sorted({r["Counter_Name"] for r in rows})
+            for c in counters:
+                fused = [r for r in rows if r["Counter_Name"] == c and
+                         any(k in r["Kernel_Name"] for k in FUSED_KERNELS)]
+                if len(fused) != n:
+                    raise SystemExit(f"{path}: {len(fused)} fused-kernel values of {c}, "
+                                     f"{n} dispatches in the phases")
+                for i, r in enumerate(fused):
+                    vals.setdefault((label_of[i], c), []).append(float(r["Counter_Value"]))
+                cp = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == c and
+                      "mfr_copy_probe_kernel" in r["Kernel_Name"]]
+                if cp:
+                    copy[c] = sum(cp) / len(cp)
+        counters = sorted({c for _, c in vals})
+        lines += ["Mean per dispatch, by phase.", "",
+                  "| phase | " + " | ".join(counters) + " |",
+                  "|---|" + "---|" * len(counters)]
+        for lab in order:
+            lines.append(f"| {lab} | " + " | ".join(
+                f"{statistics.mean(vals[(lab, c)]):,.1f}" if (lab, c) in vals else ""
+                for c in counters) + " |")
+        if "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
+            cf = (1 << 30) / (copy["FETCH_SIZE"] * 1024.0)
+            cw = (1 << 30) / (copy["WRITE_SIZE"] * 1024.0)
+            lines += ["", f"Calibrated on the 1 GiB copy probe of the same runs: FETCH_SIZE x "
+                      f"{cf:.4f}, WRITE_SIZE x {cw:.4f} (KiB per dispatch to bytes).", "",
+                      "| phase | traffic B per dispatch | algorithmic B | ratio |", "|---|---|---|---|"]
+            for lab in order:
+                if (lab, "FETCH_SIZE") in vals and (lab, "WRITE_SIZE") in vals:
+                    t = (statistics.mean(vals[(lab, "FETCH_SIZE")]) * 1024.0 * cf +
+                         statistics.mean(vals[(lab, "WRITE_SIZE")]) * 1024.0 * cw)
+                    alg = nbytes.get(lab)
+                    lines.append(f"| {lab} | {t:,.0f} | {alg:,} | {t / alg:.4f} |" if alg else
+                                 f"| {lab} | {t:,.0f} | | |")
+    if args.append_sweep:
+        lines += [""] + sweep_table_lines(args.append_sweep)
+    lines += ["", f"Kernel code hash of the library measured: `{kernel_code_hash()}`."]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def sweep_table_lines(path):
+    """The graph-timed shape sweep (the JSON line of bench.py --shape-sweep)
+    as a table: µs per call per shape and T, the fastest shape marked."""
+    with open(path) as f:
+        sw = next(json.loads(ln)["shape_sweep"] for ln in f if '"shape_sweep"' in ln)
+    ts = list(sw["T"])
+    shapes = [k for k in sw["T"][ts[0]] if k not in ("auto_path", "bytes")]
+    lines = [f"Event timing of the same shapes (`bench.py --shape-sweep`: graphs of one call per "
+             f"buffer set, median of {sw['reps']} interleaved repetitions), µs per call; the "
+             "fastest shape of each T in bold, `auto` is the library's own choice (its path in "
+             "the last row):", "",
+             "| shape | " + " | ".join(f"T = {t}" for t in ts) + " |",
+             "|---|" + "---|" * len(ts)]
+    best = {t: min(v for k, v in sw["T"][t].items() if k in shapes) for t in ts}
+    for sh in shapes:
+        cells = []
+        for t in ts:
+            v = sw["T"][t][sh]
+            cells.append(f"**{v:.2f}**" if v == best[t] else f"{v:.2f}")
+        lines.append(f"| {sh} | " + " | ".join(cells) + " |")
+    lines.append("| auto path | " + " | ".join(sw["T"][t]["auto_path"] for t in ts) + " |")
+    return lines
 
 
 def summarize_pmc(args):
@@ -1237,6 +1431,16 @@ def main():
     ap.add_argument("--sweep-reps", type=int, default=3)
     ap.add_argument("--state-run", action="store_true",
                     help="eager launches of the input-state phases, for a counter run")
+    ap.add_argument("--sweep-ts", default="", help="with --shape-sweep: comma-separated T values")
+    ap.add_argument("--eager", action="store_true",
+                    help="with --shape-sweep: eager launches for a trace; print the phase table")
+    ap.add_argument("--persist-counters-run", action="store_true",
+                    help="automatic and persistent launches at T = 512, 2048, 8192, then the copy")
+    ap.add_argument("--summarize-phases", action="store_true")
+    ap.add_argument("--phases-json", help="with --summarize-phases: stdout of the phase run")
+    ap.add_argument("--trace-csv", help="with --summarize-phases: a kernel_trace.csv")
+    ap.add_argument("--append-sweep", default="",
+                    help="with --summarize-phases: stdout of bench.py --shape-sweep, as a table")
     ap.add_argument("--latency-run", action="store_true")
     ap.add_argument("--summarize-trace")
     ap.add_argument("--kernel-filter", default="mfr_")
@@ -1262,6 +1466,8 @@ def main():
         return summarize_counters(args)
     if args.summarize_pmc_variants:
         return summarize_pmc_variants(args)
+    if args.summarize_phases:
+        return summarize_phases(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the fused op has no cross-GPU step to time here "
@@ -1278,6 +1484,8 @@ def main():
         return run_sweep(args)
     if args.state_run:
         return run_states(args)
+    if args.persist_counters_run:
+        return run_persist_counters(args)
     return run_bench(args)
 
 

@@ -269,3 +269,62 @@ def test_cpu_baseline_all_cores_covers_every_token(monkeypatch):
         got = np.concatenate([s for s in seen[p * n:(p + 1) * n] if s.size], axis=0)
         assert np.array_equal(np.sort(got, axis=None), np.sort(d["perm_idx"], axis=None))
         assert got.shape == d["perm_idx"].shape
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_summarize_phases_maps_dispatches_by_order(tmp_path):
+    """Phase runs label the fused-kernel dispatches by their position: the
+    trace summary attributes durations, and the counter summary values and
+    calibrated traffic, to the right phase; other kernels (cache scrubs, the
+    copy probe) are left out of the count."""
+    phases = {"phases": [{"label": "T512/auto", "dispatches": 2, "bytes": 1000},
+                         {"label": "T512/persist", "dispatches": 1, "bytes": 1000}]}
+    pj = tmp_path / "phases.json"
+    pj.write_text("noise line\n" + json.dumps(phases) + "\n")
+    fused = "void mfr::mfr_fused_kernel<3, 8, 0, 0, false>(int const*)"
+    persist = "void mfr::mfr_persist_kernel<8, 0, 0, false>(int const*)"
+    trace = tmp_path / "trace.csv"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp",
+           "End_Timestamp"]
+    _write_csv(trace, hdr, [[3, persist, 196608, 768, 5000, 8000],
+                            [1, fused, 131072, 256, 1000, 2000],
+                            [0, "mfr_touch_probe_kernel", 1024, 256, 0, 10],
+                            [2, fused, 131072, 256, 3000, 5000]])
+    out = tmp_path / "t.md"
+    bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=str(trace),
+                                              counter_csv=[], title="t", command="c",
+                                              out=str(out), append_sweep=""))
+    text = out.read_text()
+    row_auto = next(ln for ln in text.splitlines() if ln.startswith("| T512/auto"))
+    row_persist = next(ln for ln in text.splitlines() if ln.startswith("| T512/persist"))
+    assert "| 2 | 1.50 |" in row_auto and "mfr_fused_kernel" in row_auto
+    assert "| 1 | 3.00 |" in row_persist and "mfr_persist_kernel" in row_persist
+    # counters: 2 counters per dispatch, plus the copy probe for calibration
+    cnt = tmp_path / "c.csv"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for i, (k, fv, wv) in enumerate([(fused, 400, 200), (fused, 600, 200), (persist, 500, 300)]):
+        rows += [[i, k, "FETCH_SIZE", fv / 1024.0], [i, k, "WRITE_SIZE", wv / 1024.0]]
+    rows += [[9, "mfr_copy_probe_kernel", "FETCH_SIZE", (1 << 30) / 1024.0 / 2],
+             [9, "mfr_copy_probe_kernel", "WRITE_SIZE", (1 << 30) / 1024.0]]
+    _write_csv(cnt, hdr, rows)
+    bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=None,
+                                              counter_csv=[str(cnt)], title="t", command="c",
+                                              out=str(out), append_sweep=""))
+    lines = out.read_text().splitlines()
+    # fetch scaled by 2 (the copy's fetch counts half), write by 1
+    assert any(ln.startswith("| T512/auto | 1,200 | 1,000 | 1.2000 |") for ln in lines), lines
+    assert any(ln.startswith("| T512/persist | 1,300 | 1,000 | 1.3000 |") for ln in lines), lines
+    # a mismatch between the phase table and the dispatches is refused
+    _write_csv(trace, ["Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Workgroup_Size_X",
+                       "Start_Timestamp", "End_Timestamp"], [[0, fused, 1, 1, 0, 1]])
+    with pytest.raises(SystemExit):
+        bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=str(trace),
+                                                  counter_csv=[], title="t", command="c",
+                                                  out=str(out), append_sweep=""))
