@@ -5,17 +5,19 @@ One step = one call of the fused op over one batch of synthetic input (all of
 its steps: gather, weighted sum, shared and residual adds, rounding, RMSNorm).
 The headline workload is the 8192-token prefill chunk (H=6144, K=8, scale 2.5,
 1% of residual rows x100; 1.21 GB per call, larger than the 256 MB Infinity
-Cache, so every call streams from HBM). Inputs are resident in HBM before the
-timed region; HIP events on the launch stream bracket exactly --steps calls.
+Cache, so every call streams its inputs from HBM). Inputs are resident in HBM
+before the timed region; HIP events on the launch stream bracket exactly
+--steps calls on one buffer set.
 
 Printed (stdout, one JSON line): effective HBM GB/s = algorithmic bytes per
 call / time per call, the roofline object for the fused kernel, the oracle's
 CPU baseline on the same workload (one core, and every core in threads over
 disjoint token ranges), and, as context, decode-latency figures for
 T = 1..64 and the 512-token batch, a measured copy ceiling, the dense tail and
-the FP8-output calls at T = 8192, the host cost of the torch deferred path, and
+the FP8-output calls at T = 8192, the host cost of the torch deferred path,
 the headline workload with its gathered rows grouped by expert instead of
-randomly placed.
+randomly placed, and the chunk and the batch in other input states (buffer
+sets cycled, outputs and inputs cycled apart, Infinity Cache flushed).
 
 Modes used with rocprofv3 (see profiles/):
   --pmc-run          a short run of the fused kernel plus a 1 GiB copy of known
@@ -23,7 +25,15 @@ Modes used with rocprofv3 (see profiles/):
   --latency-run      eager calls at the decode sizes and the 512 batch (and the
                      dense, FP8-output and dense FP8-output calls at T=28 and
                      8192), to trace
+  --shape-sweep      every launch shape (vectors per thread x store policy, and
+                     the persistent kernel) at T = 64..8192, HBM-cold; with
+                     --eager, plain launches for a kernel trace
+  --persist-counters-run  the automatic and the persistent launch at T = 512,
+                     2048 and 8192, then the copy probe, for counters
+  --state-run        eager launches of the input states, for counters
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
+  --summarize-phases durations or counters of a phase run (shape sweep,
+                     persistent counters, input states) by dispatch order
   --summarize-pmc    turn counter_collection.csv files into profiles/ traffic data
   --pmc-variants-run the dense tail, the FP8-output call and the dense tail with
                      FP8 output at T=8192, plus the copy probe, for the same
@@ -821,23 +831,53 @@ def run_sweep(args):
 # per set and graph); see input_states().
 STATE_PHASES = (
     ("prefill_T8192_1set", 8192, 1, 8),
+    ("prefill_T8192_1set_cache_flushed", 8192, 1, 4),
     ("prefill_T8192_2sets", 8192, 2, 4),
     ("prefill_T8192_4sets", 8192, 4, 2),
+    ("prefill_T8192_1input_2outputs", 8192, (1, 2), 4),
+    ("prefill_T8192_2inputs_1output", 8192, (2, 1), 4),
     ("batch_T512_8sets_graph64", 512, 8, 8),
     ("batch_T512_32sets_graph64", 512, 32, 2),
     ("batch_T512_8sets_graph8", 512, 8, 1),
 )
 
 
+def mixed_calls(d, n_in, n_out):
+    """Closures for the fused op that cycle n_in input sets and n_out output
+    sets independently (call j reads input set j % n_in and writes output set
+    j % n_out), max(n_in, n_out) of them, with n_in, n_out in {1, 2}."""
+    import torch
+    import top_finalize_residual_amd as mfr
+    sets = [to_device(d) for _ in range(n_in)]
+    T, K = sets[0]["perm_idx"].shape
+    H = sets[0]["gamma"].shape[0]
+    outs = [(torch.empty_like(sets[0]["residual"]), torch.empty_like(sets[0]["residual"]))
+            for _ in range(n_out)]
+    names = ("expert_out", "perm_idx", "topk_w", "shared_out", "residual", "gamma")
+    calls = []
+    for j in range(max(n_in, n_out)):
+        a = [sets[j % n_in][k].data_ptr() for k in names]
+        r, n = (t.data_ptr() for t in outs[j % n_out])
+
+        def call(a=a, r=r, n=n):
+            _raise_on(mfr.moe_finalize_rmsnorm_raw(*a, d["eps"], d["scale"], r, n, T, H, K,
+                                                   torch.cuda.current_stream().cuda_stream))
+        call.keep = (sets, outs)
+        calls.append(call)
+    return calls
+
+
 def _state_sets(cache, T, n, inputs):
-    """n device copies of the workload at T (shared between phases)."""
+    """Calls over n device copies of the workload at T (shared between
+    phases), or over (inputs, outputs) copies cycled independently."""
     import synth
     cfg = "prefill" if T == 8192 else "batch512"
     key = (T, n)
     if key not in cache:
         if T not in inputs:
             inputs[T] = synth.config_inputs(cfg, T)
-        cache[key] = stacked_calls(inputs[T], n, "bf16")
+        cache[key] = (mixed_calls(inputs[T], *n) if isinstance(n, tuple) else
+                      stacked_calls(inputs[T], n, "bf16"))
     return cache[key]
 
 
@@ -845,31 +885,57 @@ def input_states(reps=3, eager=False, log_phase=None, prefill=None):
     """The fused op at T = 8192 and 512 in the input states its bandwidth
     depends on: one buffer set re-read call after call, or several distinct
     sets cycled (1, 2 and 4 sets of 1.41 GB at T = 8192; 8 and 32 sets of
-    75.5 MB at T = 512). Each phase times graphs of n_sets x per_set calls
+    75.5 MB at T = 512); one set re-read with the Infinity Cache flushed
+    before every call (512 MB of unrelated reads; each call then timed alone
+    with events); and inputs and outputs cycled apart (one input set with two
+    output sets, two input sets with one output set). Each other phase times graphs of n_sets x per_set calls
     (median of reps), or, with eager, plain launches in the same order (for
     a counter run, whose dispatches then map to phases by position)."""
     import synth
     cache = {}
     inputs = {} if prefill is None else {8192: prefill}
     out = {}
+    import torch
     for name, T, n, per_set in STATE_PHASES:
         calls = _state_sets(cache, T, n, inputs)
         nb = synth.config_algorithmic_bytes("prefill" if T == 8192 else "batch512", T)
+        flushed = name.endswith("_cache_flushed")
         if eager:
             for _ in range(per_set):
                 for c in calls:
+                    if flushed:
+                        scrub_infinity_cache()
                     c()
-            import torch
             torch.cuda.synchronize()
             if log_phase:
-                log_phase(name, per_set * n)
+                log_phase(name, per_set * len(calls))
             continue
         scrub_infinity_cache()
+        if flushed:
+            # one call at a time, each after 512 MB of unrelated reads, timed
+            # alone with events on its stream
+            st = torch.cuda.current_stream()
+            ts = []
+            for _ in range(2 * per_set + 1):
+                scrub_infinity_cache()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                calls[0]()
+                e1.record(st)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            ts.sort()
+            us = ts[len(ts) // 2]
+            out[name] = {"us": round(us, 2),
+                         "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "input_sets": 1,
+                         "output_sets": 1, "calls_per_graph": None}
+            continue
         ts = sorted(time_graph(calls, per_set, 3) * 1e3 for _ in range(reps))
         us = ts[len(ts) // 2]
+        n_in, n_out = n if isinstance(n, tuple) else (n, n)
         out[name] = {"us": round(us, 2), "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                     "sets": n, "footprint_gb": round(n * nb / 1e9, 2),
-                     "calls_per_graph": n * per_set}
+                     "input_sets": n_in, "output_sets": n_out,
+                     "calls_per_graph": len(calls) * per_set}
         if T == 8192 and n == 4:
             del cache[(T, 1)], cache[(T, 2)]  # keep the device footprint bounded
     return out
@@ -987,7 +1053,8 @@ def run_bench(args):
            "us_per_call": round(ms * 1e3, 2), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": "prefill chunk: T=8192 tokens, H=6144, K=8, scale 2.5, "
-                                  "1% residual rows x100 (1.21 GB per call, HBM-cold)",
+                                  "1% residual rows x100 (1.21 GB per call; one buffer set, "
+                                  "calls back to back; other input states in input_states)",
                       "T": d["T"], "H": d["H"], "K": d["K"], "algorithmic_bytes": nbytes,
                       "path": {1: "token", 2: "stream"}.get(path, "?"),
                       "parallelism": "single GPU"}}
@@ -1186,6 +1253,32 @@ def summarize_phases(args):
             lines.append(f"| {lab} | " + " | ".join(
                 f"{statistics.mean(vals[(lab, c)]):,.1f}" if (lab, c) in vals else ""
                 for c in counters) + " |")
+        derived = [
+            ("UTCL1 translation misses per request", "TCP_UTCL1_TRANSLATION_MISS_sum",
+             "TCP_UTCL1_REQUEST_sum", 1.0, "{:.2e}"),
+            ("TCP to L2 mean read latency (cycles)", "TCP_TCC_READ_REQ_LATENCY_sum",
+             "TCP_TCC_READ_REQ_sum", 1.0, "{:,.0f}"),
+            ("L2 to memory mean read latency (cycles)", "TCC_EA0_RDREQ_LEVEL_sum",
+             "TCC_EA0_RDREQ_sum", 1.0, "{:,.0f}"),
+            ("UTCL2 busy share of GPU-active cycles", "GRBM_UTCL2_BUSY", "GRBM_GUI_ACTIVE", 1.0,
+             "{:.4f}"),
+        ]
+        have = [d for d in derived if any((lab, d[1]) in vals and (lab, d[2]) in vals
+                                          for lab in order)]
+        if have:
+            lines += ["", "Derived, per phase (ratios of the per-dispatch means above):", "",
+                      "| phase | " + " | ".join(d[0] for d in have) + " |",
+                      "|---|" + "---|" * len(have)]
+            for lab in order:
+                cells = []
+                for _, num, den, k, fmt in have:
+                    if (lab, num) in vals and (lab, den) in vals:
+                        d_ = statistics.mean(vals[(lab, den)])
+                        cells.append(fmt.format(k * statistics.mean(vals[(lab, num)]) / d_)
+                                     if d_ else "")
+                    else:
+                        cells.append("")
+                lines.append(f"| {lab} | " + " | ".join(cells) + " |")
         if "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
             cf = (1 << 30) / (copy["FETCH_SIZE"] * 1024.0)
             cw = (1 << 30) / (copy["WRITE_SIZE"] * 1024.0)
@@ -1201,10 +1294,39 @@ def summarize_phases(args):
                                  f"| {lab} | {t:,.0f} | | |")
     if args.append_sweep:
         lines += [""] + sweep_table_lines(args.append_sweep)
+    if args.append_states:
+        lines += [""] + states_table_lines(args.append_states)
     lines += ["", f"Kernel code hash of the library measured: `{kernel_code_hash()}`."]
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_sweep(args):
+    """A profiles/ page from the JSON line of bench.py --shape-sweep alone."""
+    lines = [f"# {args.title}", "", "Commands ($REPO is the repository root, $OUT any output "
+             "directory):", "", "```", args.command, "```", ""] + sweep_table_lines(
+                 args.summarize_sweep) + ["", f"Kernel code hash of the library measured: "
+                                              f"`{kernel_code_hash()}`."]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def states_table_lines(path):
+    """The input_states figures of a bench.py JSON line as a table."""
+    with open(path) as f:
+        st = next(json.loads(ln)["input_states"] for ln in f if '"input_states"' in ln)
+    lines = ["Event timing of the same states in the benchmark run (`input_states` of the "
+             "bench.py JSON line; graphs of the listed number of calls, median of 3, except "
+             "the flushed state, timed one call at a time after 512 MB of unrelated reads):", "",
+             "| state | input sets | output sets | calls per graph | µs per call | "
+             "% of 8 TB/s |", "|---|---|---|---|---|---|"]
+    for name, v in st.items():
+        lines.append(f"| {name} | {v['input_sets']} | {v['output_sets']} | "
+                     f"{v['calls_per_graph'] or 'one at a time'} | {v['us']:.2f} | "
+                     f"{100 * v['frac']:.1f} |")
+    return lines
 
 
 def sweep_table_lines(path):
@@ -1441,6 +1563,10 @@ def main():
     ap.add_argument("--trace-csv", help="with --summarize-phases: a kernel_trace.csv")
     ap.add_argument("--append-sweep", default="",
                     help="with --summarize-phases: stdout of bench.py --shape-sweep, as a table")
+    ap.add_argument("--summarize-sweep", default="",
+                    help="stdout of bench.py --shape-sweep: write it as a profiles/ table")
+    ap.add_argument("--append-states", default="",
+                    help="with --summarize-phases: a bench.py JSON line; its input_states table")
     ap.add_argument("--latency-run", action="store_true")
     ap.add_argument("--summarize-trace")
     ap.add_argument("--kernel-filter", default="mfr_")
@@ -1468,6 +1594,8 @@ def main():
         return summarize_pmc_variants(args)
     if args.summarize_phases:
         return summarize_phases(args)
+    if args.summarize_sweep:
+        return summarize_sweep(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the fused op has no cross-GPU step to time here "

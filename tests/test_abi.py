@@ -63,7 +63,8 @@ def test_path_query():
     assert mfr.moe_finalize_rmsnorm_path(28, 6144, 8) == mfr.PATH_TOKEN
     assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_STREAM
     assert mfr.moe_finalize_rmsnorm_path(256, 6144, 8) == mfr.PATH_TOKEN
-    assert mfr.moe_finalize_rmsnorm_path(257, 6144, 8) == mfr.PATH_STREAM
+    assert mfr.moe_finalize_rmsnorm_path(511, 6144, 8) == mfr.PATH_TOKEN
+    assert mfr.moe_finalize_rmsnorm_path(512, 6144, 8) == mfr.PATH_STREAM
     assert mfr.moe_finalize_rmsnorm_path(512, 6144, 8) == mfr.PATH_STREAM
     assert mfr.moe_finalize_rmsnorm_path(0, 6144, 8) == mfr.PATH_TOKEN
     for bad in ((-1, 6144, 8), (4, 6143, 8), (4, 0, 8), (4, 16392, 8), (4, 6144, 0),

@@ -299,7 +299,7 @@ def test_summarize_phases_maps_dispatches_by_order(tmp_path):
     out = tmp_path / "t.md"
     bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=str(trace),
                                               counter_csv=[], title="t", command="c",
-                                              out=str(out), append_sweep=""))
+                                              out=str(out), append_sweep="", append_states=""))
     text = out.read_text()
     row_auto = next(ln for ln in text.splitlines() if ln.startswith("| T512/auto"))
     row_persist = next(ln for ln in text.splitlines() if ln.startswith("| T512/persist"))
@@ -316,7 +316,7 @@ def test_summarize_phases_maps_dispatches_by_order(tmp_path):
     _write_csv(cnt, hdr, rows)
     bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=None,
                                               counter_csv=[str(cnt)], title="t", command="c",
-                                              out=str(out), append_sweep=""))
+                                              out=str(out), append_sweep="", append_states=""))
     lines = out.read_text().splitlines()
     # fetch scaled by 2 (the copy's fetch counts half), write by 1
     assert any(ln.startswith("| T512/auto | 1,200 | 1,000 | 1.2000 |") for ln in lines), lines
@@ -327,4 +327,4 @@ def test_summarize_phases_maps_dispatches_by_order(tmp_path):
     with pytest.raises(SystemExit):
         bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=str(trace),
                                                   counter_csv=[], title="t", command="c",
-                                                  out=str(out), append_sweep=""))
+                                                  out=str(out), append_sweep="", append_states=""))

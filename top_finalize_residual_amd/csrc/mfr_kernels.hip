@@ -703,10 +703,13 @@ constexpr int kVptMax = 4;
 // Row bound of the entry points that are not told R: 2^31, above every
 // non-negative int32 index, so no slot is ever treated as past the rows.
 constexpr uint32_t kNoRowBound = 0x80000000u;
-// Token counts up to this use the token path (widest workgroup per token).
-// Measured on MI355X at H = 6144: the token path is ahead up to T = 256, the
-// 256-thread stream shape from T = 512.
-constexpr int64_t kTokenPathMaxT = 256;
+// Token counts up to this use the token path (widest workgroup per token),
+// that is below two tokens per CU on the 256 CUs of an MI355X. Measured there
+// at H = 6144 (HBM-cold, every shape interleaved, median of 5): the widest
+// workgroup is 1-4% faster than the 256-thread stream shape from T = 257 to
+// 448 and level with it at 511 and 512; from T = 768 the stream shape is
+// ahead.
+constexpr int64_t kTokenPathMaxT = 511;
 // Output bytes (both outputs) from which the stores write through. Measured on
 // MI355X at H = 6144: write-back wins at T = 512 (12.6 MB of outputs, which
 // the 32 MB of L2 absorbs), write-through from T = 1024 (25 MB) up.
