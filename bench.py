@@ -27,7 +27,10 @@ Modes used with rocprofv3 (see profiles/):
                      8192), to trace
   --shape-sweep      every launch shape (vectors per thread x store policy, and
                      the persistent kernel) at T = 64..8192, HBM-cold; with
-                     --eager, plain launches for a kernel trace
+                     --alternatives, the alternatives to the shipped launch
+                     (a per-CU workgroup cap, per-XCD token ranges, every
+                     store encoding, the persistent kernel) at T = 512..8192;
+                     with --eager, plain launches for a kernel trace
   --persist-counters-run  the automatic and the persistent launch at T = 512,
                      2048 and 8192, then the copy probe, for counters
   --state-run        eager launches of the input states, for counters
@@ -754,77 +757,166 @@ def deferred_overhead():
 
 SWEEP_TS = (64, 256, 257, 512, 1024, 2048, 8192)
 
+# Alternatives to the shipped launch at the fused op's sizes, each reachable
+# through the tuning interface as tuning.forced(**kwargs): a cap on the
+# workgroups per CU (LDS reserved at launch), the per-XCD token ranges, every
+# output store encoding, and the persistent kernel.
+ALTERNATIVES = (
+    ("auto", {}),
+    ("no-cap", dict(residency=64)),
+    ("cap-4-per-CU", dict(residency=4)),
+    ("cap-3-per-CU", dict(residency=3)),
+    ("cap-2-per-CU", dict(residency=2)),
+    ("cap-1-per-CU", dict(residency=1)),
+    ("xcd-ranges", dict(order=1)),
+    ("store-wb", dict(store=1)),
+    ("store-wt", dict(store=2)),
+    ("store-nt", dict(store=3)),
+    ("store-nt-wt", dict(store=4)),
+    ("persist", dict(path=3)),
+)
+ALT_TS = (512, 1024, 2048, 4096, 8192)
 
-def sweep_shapes(reps=3, cold_bytes=600_000_000, phases=None, ts=SWEEP_TS):
-    """Every launch shape at the fused op's workload sizes (H = 6144, K = 8):
-    the one-token-per-workgroup kernel at 1..4 vectors per thread (768, 384,
-    256 and 192 threads) with write-back and write-through stores, and the
-    persistent kernel with both store policies, beside the automatic choice.
-    HBM-cold harness: a graph of one call on each of n buffer sets together
-    above cold_bytes (more than twice the Infinity Cache); at T = 8192 one
-    set (1.21 GB) is cold by size. The shapes are timed in turn, in forward
-    then reverse order, reps times; the median per shape is reported. The
-    token and stream paths are automatic choices among these shapes.
 
-    With phases (a list), the calls are launched eagerly instead, in the same
-    order, and each (T, shape) group is appended to phases as
-    {label, dispatches, bytes}, so that a kernel trace of the run maps its
-    dispatches to shapes by position."""
-    import torch
-    import synth
-    from top_finalize_residual_amd import tuning
+def _shape_list():
+    """The launch shapes of the shape sweep, as (name, tuning.forced kwargs)."""
     import top_finalize_residual_amd as mfr
+    from top_finalize_residual_amd import tuning
     WB, WT = tuning.STORE_WRITE_BACK, tuning.STORE_WRITE_THROUGH
-    shapes = [(f"v{v}-{'wb' if st == WB else 'wt'}", (mfr.PATH_STREAM, v, st))
+    shapes = [(f"v{v}-{'wb' if st == WB else 'wt'}", dict(path=mfr.PATH_STREAM, vpt=v, store=st))
               for v in (1, 2, 3, 4) for st in (WB, WT)]
-    shapes += [("persist-wb", (mfr.PATH_PERSIST, 0, WB)), ("persist-wt", (mfr.PATH_PERSIST, 0, WT)),
-               ("auto", (0, 0, 0))]
-    out = {"H": 6144, "K": 8, "unit": "us", "reps": reps, "T": {}}
+    shapes += [("persist-wb", dict(path=mfr.PATH_PERSIST, store=WB)),
+               ("persist-wt", dict(path=mfr.PATH_PERSIST, store=WT)), ("auto", {})]
+    return shapes
+
+
+def _sweep_workloads(ts, cold_bytes, states=False, H=6144):
+    """(label, T, nbytes, calls, calls per set and graph, flushed) of each
+    workload of a sweep at H (6144: the named workloads), K = 8. HBM-cold:
+    one call on each of n
+    buffer sets together above cold_bytes (more than twice the Infinity
+    Cache); at T = 8192 one set (1.21 GB, cold by size) called 10 times in a
+    row. With states, at T = 8192 also one input set with two output sets
+    alternated, and one set with the Infinity Cache flushed before every
+    call (flushed: each call timed alone, see _sweep)."""
+    import synth
     for T in ts:
-        cfg = "prefill" if T == 8192 else "batch512" if T == 512 else None
+        cfg = None if H != 6144 else "prefill" if T == 8192 else "batch512" if T == 512 else None
         d = synth.config_inputs(cfg, T) if cfg else synth.generate(
-            T, 6144, 8, scale=2.5, weights="top8_of_256", seed=synth.BASE_SEED + 9000 + T)
+            T, H, 8, scale=2.5, weights="top8_of_256",
+            seed=synth.BASE_SEED + 9000 + T + (0 if H == 6144 else H))
         nb = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
         n = 1 if T == 8192 else max(2, -(-cold_bytes // nb))
         calls = stacked_calls(d, n, "bf16")
-        per_call = 10 if n == 1 else 1
+        yield str(T), T, nb, calls, 10 if n == 1 else 1, False
+        if states and T == 8192:
+            yield "8192, cache flushed", T, nb, calls, 5, True
+            del calls
+            calls = mixed_calls(d, 1, 2)
+            yield "8192, 2 output sets", T, nb, calls, 5, False
+        del calls
+
+
+def _flushed_us(call, n):
+    """Median µs of n calls, each after 512 MB of unrelated reads and timed
+    alone with events on its stream."""
+    import torch
+    st = torch.cuda.current_stream()
+    ts = []
+    for _ in range(n):
+        scrub_infinity_cache()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return sorted(ts)[n // 2]
+
+
+def _sweep(workloads, shapes, reps, phases, H=6144):
+    """Times every shape on every workload: graphs of the workload's calls,
+    after a cache scrub (or, for a flushed workload, each call alone after
+    its own scrub), in forward then reverse shape order, reps times; the
+    median per shape. With phases (a list), plain launches in the same order
+    instead, each (workload, shape) group appended to phases as {label,
+    dispatches, bytes}, so that a kernel trace of the run maps its
+    dispatches to shapes by position."""
+    import torch
+    import top_finalize_residual_amd as mfr
+    from top_finalize_residual_amd import tuning
+    out = {}
+    for label, T, nb, calls, per_call, flushed in workloads:
         times = {name: [] for name, _ in shapes}
         for r in range(reps):
             order = shapes if r % 2 == 0 else shapes[::-1]
             for name, force in order:
                 scrub_infinity_cache()
-                with tuning.forced(*force):
+                with tuning.forced(**force):
                     if phases is None:
-                        times[name].append(time_graph(calls, per_call, 3) * 1e3)
+                        times[name].append(_flushed_us(calls[0], per_call) if flushed else
+                                           time_graph(calls, per_call, 3) * 1e3)
                         continue
                     for _ in range(per_call):
                         for c in calls:
+                            if flushed:
+                                scrub_infinity_cache()
                             c()
                     torch.cuda.synchronize()
-                    phases.append({"label": f"T{T}/{name}", "dispatches": per_call * len(calls),
-                                   "bytes": nb})
-        del calls
+                    phases.append({"label": f"T{label}/{name}",
+                                   "dispatches": per_call * len(calls), "bytes": nb})
         if phases is not None:
             continue
         res = {name: round(sorted(v)[len(v) // 2], 2) for name, v in times.items()}
-        auto_path = mfr.moe_finalize_rmsnorm_path(T, 6144, 8)
+        auto_path = mfr.moe_finalize_rmsnorm_path(T, H, 8)
         res["auto_path"] = {1: "token", 2: "stream", 3: "persist"}.get(auto_path, "?")
         res["bytes"] = nb
-        out["T"][str(T)] = res
-        log(f"sweep T={T}: " + ", ".join(f"{k} {v}" for k, v in res.items() if k != "bytes"))
+        out[label] = res
+        log(f"sweep {label}: " + ", ".join(f"{k} {v}" for k, v in res.items() if k != "bytes"))
     return out
+
+
+def sweep_shapes(reps=3, cold_bytes=600_000_000, phases=None, ts=SWEEP_TS):
+    """Every launch shape at the fused op's workload sizes (H = 6144, K = 8):
+    the one-token-per-workgroup kernel at 1..4 vectors per thread (768, 384,
+    256 and 192 threads) with write-back and write-through stores, and the
+    persistent kernel with both store policies, beside the automatic choice,
+    in the HBM-cold harness of _sweep_workloads. The token and stream paths
+    are automatic choices among these shapes.
+
+    With phases (a list), the calls are launched eagerly instead (see
+    _sweep)."""
+    res = _sweep(_sweep_workloads(ts, cold_bytes), _shape_list(), reps, phases)
+    return {"kind": "shapes", "H": 6144, "K": 8, "unit": "us", "reps": reps, "T": res}
+
+
+def sweep_alternatives(reps=5, cold_bytes=600_000_000, phases=None, ts=ALT_TS, H=6144):
+    """The alternatives to the shipped launch (ALTERNATIVES) in the same
+    harness, at T = 512..8192, and at T = 8192 also with the Infinity Cache
+    flushed before every call and with two output sets alternated (the
+    outputs then never meet their own lines in the Infinity Cache)."""
+    res = _sweep(_sweep_workloads(ts, cold_bytes, states=True, H=H), list(ALTERNATIVES), reps,
+                 phases, H=H)
+    return {"kind": "alternatives", "H": H, "K": 8, "unit": "us", "reps": reps, "T": res}
 
 
 def run_sweep(args):
     import torch
     torch.cuda.set_device(0)
-    ts = tuple(int(x) for x in args.sweep_ts.split(",")) if args.sweep_ts else SWEEP_TS
+    alt = args.alternatives
+    default_ts = ALT_TS if alt else SWEEP_TS
+    ts = tuple(int(x) for x in args.sweep_ts.split(",")) if args.sweep_ts else default_ts
+    kw = dict(reps=args.sweep_reps, ts=ts)
+    if alt:
+        fn, kw["H"] = sweep_alternatives, args.sweep_h
+    else:
+        fn = sweep_shapes
     if args.eager:
         phases = []
-        sweep_shapes(reps=args.sweep_reps, phases=phases, ts=ts)
+        fn(phases=phases, **kw)
         print(json.dumps({"phases": phases}), flush=True)
         return
-    print(json.dumps({"shape_sweep": sweep_shapes(reps=args.sweep_reps, ts=ts)}), flush=True)
+    print(json.dumps({"shape_sweep": fn(**kw)}), flush=True)
 
 
 # Input states of the bandwidth figures: (name, T, buffer sets cycled, calls
@@ -1336,11 +1428,18 @@ def sweep_table_lines(path):
         sw = next(json.loads(ln)["shape_sweep"] for ln in f if '"shape_sweep"' in ln)
     ts = list(sw["T"])
     shapes = [k for k in sw["T"][ts[0]] if k not in ("auto_path", "bytes")]
-    lines = [f"Event timing of the same shapes (`bench.py --shape-sweep`: graphs of one call per "
-             f"buffer set, median of {sw['reps']} interleaved repetitions), µs per call; the "
-             "fastest shape of each T in bold, `auto` is the library's own choice (its path in "
-             "the last row):", "",
-             "| shape | " + " | ".join(f"T = {t}" for t in ts) + " |",
+    alt = sw.get("kind") == "alternatives"
+    what, flag = ("alternatives", "--shape-sweep --alternatives") if alt else ("shapes",
+                                                                            "--shape-sweep")
+    lines = [f"Event timing of the same {what} at H = {sw['H']}, K = {sw['K']} "
+             f"(`bench.py {flag}`: graphs of one call per "
+             f"buffer set, or of 10 calls on one set at T = 8192 and 5 calls over two output "
+             f"sets; with the cache flushed, the median of 5 calls each timed alone after 512 MB "
+             f"of unrelated reads; median of {sw['reps']} interleaved repetitions), µs per call; "
+             "the fastest "
+             "of each column in bold, `auto` is the library's own choice (its path in the last "
+             "row):", "",
+             "| " + what[:-1] + " | " + " | ".join(f"T = {t}" for t in ts) + " |",
              "|---|" + "---|" * len(ts)]
     best = {t: min(v for k, v in sw["T"][t].items() if k in shapes) for t in ts}
     for sh in shapes:
@@ -1551,6 +1650,11 @@ def main():
     ap.add_argument("--shape-sweep", action="store_true",
                     help="time every launch shape at T = 64..8192 (H=6144, K=8), HBM-cold")
     ap.add_argument("--sweep-reps", type=int, default=3)
+    ap.add_argument("--sweep-h", type=int, default=6144,
+                    help="with --shape-sweep --alternatives: the hidden size")
+    ap.add_argument("--alternatives", action="store_true",
+                    help="with --shape-sweep: the alternatives to the shipped launch (per-CU cap, "
+                         "per-XCD token ranges, store encodings, persistent) at T = 512..8192")
     ap.add_argument("--state-run", action="store_true",
                     help="eager launches of the input-state phases, for a counter run")
     ap.add_argument("--sweep-ts", default="", help="with --shape-sweep: comma-separated T values")

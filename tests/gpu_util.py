@@ -44,14 +44,14 @@ forced = tuning.forced  # force a launch configuration on this thread, automatic
 
 
 def run(dd, eps, scale, path=0, vpt=0, store=0, residual_out=None, normed_out=None, api="c",
-        residency=0):
+        residency=0, order=0):
     """One call on device tensors; returns host uint16 (residual_out, normed_out).
 
     api="c": the plain C entry point moe_finalize_rmsnorm on the tensors'
     addresses (the call the benchmark times); api="binding": the tensor-level
     binding, which goes through the checked entry point with R =
     expert_out.shape[0]."""
-    with forced(path, vpt, store, residency):
+    with forced(path, vpt, store, residency, order):
         if api == "binding":
             r, n = mfr.moe_finalize_rmsnorm(dd["expert_out"], dd["perm_idx"], dd["topk_w"],
                                             dd["shared_out"], dd["residual"], dd["gamma"], eps,

@@ -48,7 +48,11 @@ int main() {
         if (!moe_finalize_rmsnorm_strerror(c)) expect(0, 1, "strerror returns text");
     expect(mfr_tuning_force_launch(4, 0, 0), MFR_ERR_ARG, "force bad path");
     expect(mfr_tuning_force_launch(0, 5, 0), MFR_ERR_ARG, "force bad vpt");
-    expect(mfr_tuning_force_launch(0, 0, 3), MFR_ERR_ARG, "force bad store");
+    expect(mfr_tuning_force_launch(0, 0, 5), MFR_ERR_ARG, "force bad store");
+    expect(mfr_tuning_force_token_order(2), MFR_ERR_ARG, "force bad token order");
+    expect(mfr_tuning_force_residency(-1), MFR_ERR_ARG, "force bad residency");
+    expect(mfr_tuning_force_token_order(MFR_ORDER_XCD_RANGES), MFR_OK, "force token order");
+    expect(mfr_tuning_force_token_order(MFR_ORDER_DEFAULT), MFR_OK, "token order reset");
     expect(mfr_tuning_force_launch(MFR_PATH_STREAM, 2, MFR_STORE_WRITE_THROUGH), MFR_OK, "force");
     expect(moe_finalize_rmsnorm_path(1, 6144, 8), MFR_PATH_STREAM, "forced path");
     expect(mfr_tuning_force_launch(0, 0, 0), MFR_OK, "force reset");

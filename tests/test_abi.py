@@ -83,10 +83,17 @@ def test_launch_override_validates_and_is_per_thread():
         assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_STREAM
         tuning.force_launch(mfr.PATH_TOKEN, 2, 0)
         assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
-        for bad in ((4, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 3), (0, 0, -1)):
+        for bad in ((4, 0, 0), (-1, 0, 0), (0, 5, 0), (0, -1, 0), (0, 0, 5), (0, 0, -1)):
             with pytest.raises(mfr.MFRError) as e:
                 tuning.force_launch(*bad)
             assert e.value.status == binding.MFR_ERR_ARG
+        for bad in (-1, 2):
+            with pytest.raises(mfr.MFRError) as e:
+                tuning.force_token_order(bad)
+            assert e.value.status == binding.MFR_ERR_ARG
+        with pytest.raises(mfr.MFRError) as e:
+            tuning.force_residency(-1)
+        assert e.value.status == binding.MFR_ERR_ARG
         # a rejected override leaves the previous one in place
         assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
         seen = []
@@ -97,6 +104,23 @@ def test_launch_override_validates_and_is_per_thread():
     finally:
         tuning.force_launch(0, 0, 0)
     assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_STREAM
+
+
+def test_forced_restores_every_knob():
+    """tuning.forced nests: on exit the enclosing override is back, token
+    order and residency included, and a forced() of nothing keeps it."""
+    with tuning.forced(mfr.PATH_TOKEN, 2, tuning.STORE_NONTEMPORAL, residency=2,
+                       order=tuning.ORDER_XCD_RANGES):
+        outer = tuning._current()
+        assert outer == ((mfr.PATH_TOKEN, 2, tuning.STORE_NONTEMPORAL), 2, tuning.ORDER_XCD_RANGES)
+        with tuning.forced(mfr.PATH_STREAM, 0, 0, residency=1):
+            assert tuning._current() == ((mfr.PATH_STREAM, 0, 0), 1, 0)
+            assert mfr.moe_finalize_rmsnorm_path(1, 6144, 8) == mfr.PATH_STREAM
+        assert tuning._current() == outer
+        with tuning.forced():
+            assert tuning._current() == outer
+        assert mfr.moe_finalize_rmsnorm_path(8192, 6144, 8) == mfr.PATH_TOKEN
+    assert tuning._current() == ((0, 0, 0), 0, 0)
 
 
 def test_public_header_has_no_launch_override():

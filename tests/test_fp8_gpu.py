@@ -38,12 +38,12 @@ def e4m3_values(codes):
     return t.to(torch.float64).numpy()
 
 
-def run_fp8(dd, d, path=0, vpt=0, store=0, bf16_normed=False, api="c", residency=0):
+def run_fp8(dd, d, path=0, vpt=0, store=0, bf16_normed=False, api="c", residency=0, order=0):
     """One FP8-output call; returns host (residual_out, codes, scales, normed_out
     or None). api="c": the plain C entry point moe_finalize_rmsnorm_fp8 (the
     call the benchmark times); api="binding": the tensor-level binding, which
     goes through the checked entry point."""
-    with gu.forced(path, vpt, store, residency):
+    with gu.forced(path, vpt, store, residency, order):
         if api == "binding":
             r, q, sc, n = mfr.moe_finalize_rmsnorm_fp8(
                 dd["expert_out"], dd["perm_idx"], dd["topk_w"], dd["shared_out"], dd["residual"],

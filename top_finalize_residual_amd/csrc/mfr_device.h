@@ -49,6 +49,10 @@ constexpr int kAuxActIn = kAuxStream;       // shared and residual rows (read on
 constexpr int kAuxGamma = kAuxDefault;      // gamma (re-read by every workgroup)
 constexpr int kAuxOut = kAuxDefault;        // outputs that fit in L2: write-back
 constexpr int kAuxWriteThrough = kAuxSc1;   // outputs larger than L2: write-through
+// Output encodings reachable only through the tuning interface (measured
+// slower than the two above).
+constexpr int kAuxOutNt = kAuxStream;
+constexpr int kAuxOutNtWriteThrough = kAuxStream | kAuxSc1;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),

@@ -62,16 +62,22 @@ struct Params {
     const u32x4* gamma;
     u32x4* residual_out;
     u32x4* normed_out;
-    int64_t T;
     float eps;
     float scale;
-    float h_f;  // H as float (exact: H <= 16384)
-    int V;      // 16-byte vectors per row, H / 8
-    int K;
+    uint32_t rows;  // rows of expert_out, at most 2^31: an index at or past it is masked
+    float h_f;      // H as float (exact: H <= 16384)
+    int64_t T;
     uint8_t* normed_fp8;  // [T, H] E4M3 codes (FP8 output modes only)
     float* fp8_scale;     // [T] per-token scales (FP8 output modes only)
-    uint32_t rows;        // rows of expert_out, at most 2^31: an index at or past it is masked
     int32_t* bad_index;   // optional: set to 1 when some slot's index is at or past R
+    // Last, so that the kernels' scalar loads of the fields above, which
+    // they use, do not take in these, which they get as leading arguments.
+    // (The order above serves the same end: a run of three used 32-bit
+    // fields is loaded as four, and a register filled with an unused field
+    // may be reused at once, which waits for the load. rows, used only by
+    // the checked kernels, therefore sits between scale and h_f.)
+    int V;  // 16-byte vectors per row, H / 8
+    int K;
 };
 
 // What the normalisation writes: the bf16 normed row, the per-token FP8
@@ -89,6 +95,16 @@ struct Lds {
     float redm[MAX_WAVES];     // maxima of |y| (range rescue, FP8 modes)
 };
 
+// Threads per workgroup at VPT vectors per thread: a row's V vectors spread
+// over whole waves. The host launches exactly this many, so the kernels
+// derive it from V (an argument they hold in registers from the start)
+// instead of reading the workgroup size from the dispatch's implicit
+// arguments, a scalar memory load ahead of the first row load.
+template <int VPT>
+__device__ __forceinline__ int threads_of(int V) {
+    return ((V + VPT - 1) / VPT + 63) & ~63;
+}
+
 // The fp32 normalisation is used when mean(s^2) + eps lies in
 // [kRescueBelow, FLT_MAX]. Above, the fp32 sum of squares has overflowed;
 // below, fp32 subnormal squares (or squares flushed to zero) could decide
@@ -100,7 +116,10 @@ constexpr float kFltMax = 0x1.fffffep127f;
 // Routing metadata of slots [k0, k0 + 8): indices and weights, read
 // unconditionally (wave-uniform scalar loads, merged by the compiler). With
 // CHECK_K, slots at or past K re-read slot K-1 so every load stays in bounds;
-// gather_rows8 ignores them.
+// gather_rows8 ignores them. Those loads cannot be merged, and scalar loads
+// complete out of order, so any use of one waits for all that are in
+// flight: the scheduling barrier keeps every use below the last load, so
+// that the sixteen loads cost one round trip rather than one each.
 template <bool CHECK_K>
 __device__ __forceinline__ void load_meta8(const Params& p, const int32_t* prow, const float* wrow,
                                            int k0, int32_t (&idx)[8], float (&wr)[8]) {
@@ -111,6 +130,7 @@ __device__ __forceinline__ void load_meta8(const Params& p, const int32_t* prow,
         idx[kk] = prow[kc];
         wr[kk] = wrow[kc];
     }
+    if constexpr (CHECK_K) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Issues the row loads of slots [k0, k0 + 8): every load is in flight when
@@ -138,7 +158,12 @@ __device__ __forceinline__ bool issue_rows8(const Params& p, const int32_t (&idx
         // wraps to 2^31 or more) and one at or past the rows.
         const bool in_range = ROWS ? static_cast<uint32_t>(idx[kk]) < p.rows : idx[kk] >= 0;
         const bool use = live && in_range && (!CHECK_K || k0 + kk < p.K);
-        rows[kk] = make_rsrc(p.expert_out + static_cast<int64_t>(use ? idx[kk] : 0) * p.V,
+        // the row offset in unsigned arithmetic (a used index is >= 0): a
+        // zero extension needs nothing of the loaded value, where a sign
+        // extension, placed by the compiler right after each index load,
+        // would make every load wait for the one before
+        const uint32_t row = use ? static_cast<uint32_t>(idx[kk]) : 0u;
+        rows[kk] = make_rsrc(p.expert_out + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.V),
                              use ? rowbytes : 0u);
         const float ws = p.scale * wr[kk];
         w[kk] = use ? ws : 0.0f;
@@ -208,7 +233,7 @@ __device__ __forceinline__ void normalise_wide(const Params& p, const int64_t t,
                                                const float (&acc)[VPT][8],
                                                const uint32_t (&off)[VPT], Lds& lds) {
     const int tid = threadIdx.x;
-    const int nw = blockDim.x >> 6;
+    const int nw = threads_of<VPT>(p.V) >> 6;
     const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
     const int64_t trow = t * static_cast<int64_t>(p.V);
     const rsrc_t gm_r = make_rsrc(p.gamma, rowbytes);
@@ -302,7 +327,7 @@ __device__ __forceinline__ void finish_token(const Params& p, const int64_t t,
                                              const u32x4 (&rs)[VPT], const u32x4 (&gm)[VPT],
                                              const uint32_t (&off)[VPT], float* red, Lds& lds) {
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
+    const int nt = threads_of<VPT>(p.V);
     const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
     const int64_t trow = t * static_cast<int64_t>(p.V);
     constexpr bool DENSE = KT < 0;
@@ -473,7 +498,7 @@ __device__ __forceinline__ void finish_token(const Params& p, const int64_t t,
 template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS>
 __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t, Lds& lds) {
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
+    const int nt = threads_of<VPT>(p.V);
     const uint32_t rowbytes = static_cast<uint32_t>(p.V) * 16u;
     const int64_t trow = t * static_cast<int64_t>(p.V);
 
@@ -535,6 +560,18 @@ struct Bound {
     static constexpr int kThreads = VPT == 1 ? 1024 : 512;
 };
 
+// Token of workgroup b. The hardware hands a dispatch's workgroups to the 8
+// XCDs in turn (b to XCD b mod 8), so token b is the default (G = 0). Given
+// the grid size G instead, XCD x takes the contiguous tokens from
+// x*q + min(x, r) on (q = G / 8, r = G mod 8: the first r XCDs take q + 1
+// tokens, the others q). Both maps are bijections of [0, G) for any G,
+// whatever the XCD count, so only the placement changes.
+__device__ __forceinline__ uint32_t token_of(uint32_t b, uint32_t G) {
+    if (G == 0) return b;
+    const uint32_t q = G >> 3, r = G & 7u, x = b & 7u, i = b >> 3;
+    return x * q + (x < r ? x : r) + i;
+}
+
 // One workgroup per token. OUT_AUX is the cache policy of the output stores
 // (write-back, or write-through for outputs larger than the L2); QM the
 // OutMode of the normalised output.
@@ -544,22 +581,43 @@ struct Bound {
 // the dispatcher places them in SGPRs when the wave launches, so the routing
 // metadata load starts at once instead of behind a scalar load of the
 // argument block. The values are the same as in p; p's copies are replaced.
+// Preloading covers 14 dwords: the six pointers, V and K packed into one
+// (vk = V | K << 16; V <= 2048, K <= 16), and xcd_grid (0, or the grid size
+// for the per-XCD token ranges of token_of), which the token index, and so
+// the first load, depends on.
 template <int VPT, int KT, int OUT_AUX, int QM, bool ROWS = false>
 __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(
         const int32_t* perm_idx, const float* topk_w, const u32x4* shared_out,
-        const u32x4* residual, const u32x4* gamma, const u32x4* expert_out, int V, int K,
-        Params p) {
+        const u32x4* residual, const u32x4* gamma, const u32x4* expert_out, uint32_t vk,
+        uint32_t xcd_grid, Params p) {
     // Per-wave partial results of the row reductions; 16-byte aligned for vector reads.
     __shared__ __align__(16) Lds lds;
-    p.perm_idx = perm_idx;
-    p.topk_w = topk_w;
-    p.shared_out = shared_out;
-    p.residual = residual;
-    p.gamma = gamma;
-    p.expert_out = expert_out;
-    p.V = V;
-    p.K = K;
-    finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(p, static_cast<int64_t>(blockIdx.x), lds);
+    // Built field by field: each field of p is then a scalar load of its
+    // own, made only where the kernel uses it, rather than part of a copy of
+    // the whole block (whose wide loads would also fill registers with
+    // fields never used, and reusing those registers early would wait for
+    // the load).
+    Params q;
+    q.perm_idx = perm_idx;
+    q.topk_w = topk_w;
+    q.shared_out = shared_out;
+    q.residual = residual;
+    q.gamma = gamma;
+    q.expert_out = expert_out;
+    q.V = static_cast<int>(vk & 0xFFFFu);
+    q.K = static_cast<int>(vk >> 16);
+    q.residual_out = p.residual_out;
+    q.normed_out = p.normed_out;
+    q.T = p.T;
+    q.eps = p.eps;
+    q.scale = p.scale;
+    q.h_f = p.h_f;
+    q.rows = p.rows;
+    q.normed_fp8 = p.normed_fp8;
+    q.fp8_scale = p.fp8_scale;
+    q.bad_index = p.bad_index;
+    const uint32_t t = token_of(blockIdx.x, xcd_grid);
+    finalize_token<VPT, KT, OUT_AUX, QM, ROWS>(q, static_cast<int64_t>(t), lds);
 }
 
 
@@ -698,6 +756,8 @@ namespace {
 
 constexpr int64_t kHMax = 16384;
 constexpr int64_t kKMax = 16;
+// V (= H / 8) and K travel packed in one 32-bit kernel argument.
+static_assert(kHMax / 8 < (1 << 16) && kKMax < (1 << 16), "V and K must fit 16 bits each");
 constexpr int64_t kTMax = 2147483647;
 constexpr int kVptMax = 4;
 // Row bound of the entry points that are not told R: 2^31, above every
@@ -714,6 +774,18 @@ constexpr int64_t kTokenPathMaxT = 511;
 // MI355X at H = 6144: write-back wins at T = 512 (12.6 MB of outputs, which
 // the 32 MB of L2 absorbs), write-through from T = 1024 (25 MB) up.
 constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
+// The stream path's 256-thread, 3-vector kernel with bf16 output (3
+// workgroups per CU by its registers) runs with at most kCapPerCu workgroups
+// per CU from kCapMinT tokens on, for H above kCapMinH (up to 6144, where
+// that kernel ends). Measured on MI355X, every alternative interleaved, at
+// H = 6144: 0.3-1.6% faster from T = 2048 to 8192, with one buffer set, with
+// the Infinity Cache flushed before each call and with alternating outputs
+// alike, and level at T = 512 and 1024; at H = 5120 level or mixed (-2% to
+// +1%), so the rule stops above it. At H = 4096 (another kernel, 7 per CU) a
+// cap of 2 was slower.
+constexpr int64_t kCapMinT = 2048;
+constexpr int64_t kCapMinH = 5120;
+constexpr int kCapPerCu = 2;
 
 // The calling thread's launch override (mfr_tuning_force_launch); 0 =
 // automatic. Thread-local, so that one thread's override never changes the
@@ -721,7 +793,8 @@ constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
 thread_local int t_force_path = 0;
 thread_local int t_force_vpt = 0;
 thread_local int t_force_store = 0;
-thread_local int t_force_residency = 0;  // persistent path: workgroups per CU (0 = all that fit)
+thread_local int t_force_residency = 0;  // workgroups per CU (0 = automatic)
+thread_local int t_force_order = 0;      // an mfr_token_order value
 
 // Environment switches, read once when the library is loaded:
 //   MFR_PATH=auto|token|stream|persist  default launch path (a thread's
@@ -794,11 +867,49 @@ int choose_vpt(int path, int64_t V) {
     return kVptMax;
 }
 
-bool write_through(int path, int64_t T, int64_t H) {
+// Output store encodings: write-back, write-through (sc1), and the two
+// non-temporal ones the tuning interface can force on the top-8 bf16 kernels
+// of the grid paths.
+enum Store { kStoreWb = 0, kStoreWt = 1, kStoreNt = 2, kStoreNtWt = 3 };
+
+// Routing variant of a launch: exactly eight slots, any K, or no routed part;
+// the checked forms also bound the indices by the rows of expert_out.
+enum Variant { kTop8 = 8, kAnyK = 0, kDense = -1, kTop8Rows = 108, kAnyKRows = 100 };
+
+// Names for the MFR_LOG lines.
+const char* variant_name(Variant v) {
+    switch (v) {
+        case kTop8: return "top8";
+        case kAnyK: return "anyK";
+        case kTop8Rows: return "top8-rows";
+        case kAnyKRows: return "anyK-rows";
+        default: return "dense";
+    }
+}
+
+const char* out_name(int qm) {
+    return qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16";
+}
+
+const char* store_name(int st) {
+    switch (st) {
+        case kStoreWt: return "write-through";
+        case kStoreNt: return "nt";
+        case kStoreNtWt: return "nt-sc1";
+        default: return "write-back";
+    }
+}
+
+int store_policy(int path, int64_t T, int64_t H, Variant v, int qm) {
     const int f = t_force_store;
-    if (f == MFR_STORE_WRITE_BACK) return false;
-    if (f == MFR_STORE_WRITE_THROUGH) return true;
-    return path != MFR_PATH_TOKEN && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes;
+    if (f == MFR_STORE_WRITE_BACK) return kStoreWb;
+    if (f == MFR_STORE_WRITE_THROUGH) return kStoreWt;
+    if ((f == MFR_STORE_NONTEMPORAL || f == MFR_STORE_NONTEMPORAL_WRITE_THROUGH) && v == kTop8 &&
+        qm == mfr::kOutBf16 && path != MFR_PATH_PERSIST)
+        return f == MFR_STORE_NONTEMPORAL ? kStoreNt : kStoreNtWt;
+    return path != MFR_PATH_TOKEN && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes
+               ? kStoreWt
+               : kStoreWb;
 }
 
 bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
@@ -809,45 +920,49 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 template <int VPT, int KT, int QM, bool ROWS = false>
-const void* pick_store(bool wt) {
-    return wt ? reinterpret_cast<const void*>(
-                    &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough, QM, ROWS>)
-              : reinterpret_cast<const void*>(
-                    &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut, QM, ROWS>);
+const void* pick_store(int st) {
+    if constexpr (KT == 8 && QM == mfr::kOutBf16 && !ROWS) {
+        if (st == kStoreNt)
+            return reinterpret_cast<const void*>(
+                &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOutNt, QM, ROWS>);
+        if (st == kStoreNtWt)
+            return reinterpret_cast<const void*>(
+                &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOutNtWriteThrough, QM, ROWS>);
+    }
+    return st == kStoreWt ? reinterpret_cast<const void*>(
+                                &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxWriteThrough, QM, ROWS>)
+                          : reinterpret_cast<const void*>(
+                                &mfr::mfr_fused_kernel<VPT, KT, mfr::kAuxOut, QM, ROWS>);
 }
 
-// Routing variant of a launch: exactly eight slots, any K, or no routed part;
-// the checked forms also bound the indices by the rows of expert_out.
-enum Variant { kTop8 = 8, kAnyK = 0, kDense = -1, kTop8Rows = 108, kAnyKRows = 100 };
-
 template <int VPT, int QM>
-const void* pick_variant(Variant v, bool wt) {
+const void* pick_variant(Variant v, int st) {
     switch (v) {
-        case kTop8: return pick_store<VPT, 8, QM>(wt);
-        case kAnyK: return pick_store<VPT, 0, QM>(wt);
-        case kTop8Rows: return pick_store<VPT, 8, QM, true>(wt);
-        case kAnyKRows: return pick_store<VPT, 0, QM, true>(wt);
-        default: return pick_store<VPT, -1, QM>(wt);
+        case kTop8: return pick_store<VPT, 8, QM>(st);
+        case kAnyK: return pick_store<VPT, 0, QM>(st);
+        case kTop8Rows: return pick_store<VPT, 8, QM, true>(st);
+        case kAnyKRows: return pick_store<VPT, 0, QM, true>(st);
+        default: return pick_store<VPT, -1, QM>(st);
     }
 }
 
 template <int VPT>
-const void* pick(Variant v, bool wt, int qm) {
+const void* pick(Variant v, int st, int qm) {
     switch (qm) {
-        case mfr::kOutFp8: return pick_variant<VPT, mfr::kOutFp8>(v, wt);
-        case mfr::kOutBoth: return pick_variant<VPT, mfr::kOutBoth>(v, wt);
-        default: return pick_variant<VPT, mfr::kOutBf16>(v, wt);
+        case mfr::kOutFp8: return pick_variant<VPT, mfr::kOutFp8>(v, st);
+        case mfr::kOutBoth: return pick_variant<VPT, mfr::kOutBoth>(v, st);
+        default: return pick_variant<VPT, mfr::kOutBf16>(v, st);
     }
 }
 
-// Kernel address for (vectors per thread, routing variant, write-through
-// outputs, output mode).
-const void* kernel_for(int vpt, Variant v, bool wt, int qm) {
+// Kernel address for (vectors per thread, routing variant, store encoding,
+// output mode).
+const void* kernel_for(int vpt, Variant v, int st, int qm) {
     switch (vpt) {
-        case 1: return pick<1>(v, wt, qm);
-        case 2: return pick<2>(v, wt, qm);
-        case 3: return pick<3>(v, wt, qm);
-        default: return pick<4>(v, wt, qm);
+        case 1: return pick<1>(v, st, qm);
+        case 2: return pick<2>(v, st, qm);
+        case 3: return pick<3>(v, st, qm);
+        default: return pick<4>(v, st, qm);
     }
 }
 
@@ -919,6 +1034,57 @@ int resident_per_cu(const void* kern, int nt) {
     return n;
 }
 
+// Dynamic LDS for a grid-path launch of kern (nt threads) that leaves room
+// for at most n of its workgroups on a CU: the smallest multiple of 512 bytes
+// above an (n+1)-th of the CU's LDS, less the kernel's own. 0 (no
+// reservation) where the kernel's registers already allow no more than n, or
+// where no such size gives exactly n, as the occupancy query reports it.
+// Computed once per (kernel, threads, n) and device.
+struct LdsCap {
+    const void* kern;
+    int nt, n, dev;
+    size_t bytes;
+};
+std::mutex g_cap_mu;
+LdsCap g_cap[256];
+int g_cap_n = 0;
+
+size_t lds_for_residency_uncached(const void* kern, int nt, int n);
+
+size_t lds_for_residency(const void* kern, int nt, int n) {
+    if (n <= 0) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(g_cap_mu);
+    for (int i = 0; i < g_cap_n; ++i)
+        if (g_cap[i].kern == kern && g_cap[i].nt == nt && g_cap[i].n == n && g_cap[i].dev == dev)
+            return g_cap[i].bytes;
+    const size_t b = lds_for_residency_uncached(kern, nt, n);
+    if (g_cap_n < 256) g_cap[g_cap_n++] = {kern, nt, n, dev, b};
+    return b;
+}
+
+size_t lds_for_residency_uncached(const void* kern, int nt, int n) {
+    if (resident_per_cu(kern, nt) <= n) return 0;
+    int dev = 0, per_cu = 0, per_block = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+        return 0;
+    hipFuncAttributes a;
+    if (hipFuncGetAttributes(&a, kern) != hipSuccess) return 0;
+    const size_t total = (static_cast<size_t>(per_cu) / (n + 1) / 512 + 1) * 512;
+    if (total <= a.sharedSizeBytes || total > static_cast<size_t>(per_block)) return 0;
+    const size_t dyn = total - a.sharedSizeBytes;
+    int got = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&got, kern, nt, dyn) != hipSuccess ||
+        got != n)
+        return 0;
+    return dyn;
+}
+
 // Aliasing rule shared by the entry points: no output may overlap another
 // output or any input, except that residual_out may be exactly residual (the
 // in-place residual update). Extents are in bytes; an empty extent never
@@ -977,7 +1143,8 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     p.h_f = static_cast<float>(H);
     p.V = static_cast<int>(H / 8);
     const int path = choose_path(T, H, v == kDense ? 1 : p.K);
-    const bool wt = write_through(path, T, H);
+    const int st = store_policy(path, T, H, v, qm);
+    const bool wt = st == kStoreWt;
     if (path == MFR_PATH_PERSIST) {
         // one launch, a grid of at most T workgroups sized to what the GPU
         // holds at once; each workgroup walks its tokens
@@ -992,10 +1159,8 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
                          "moe_finalize_rmsnorm: T=%lld H=%lld K=%d variant=%s out=%s path=persist "
                          "vpt=1 threads=%d stores=%s workgroups=%lld\n",
                          static_cast<long long>(T), static_cast<long long>(H), p.K,
-                         v == kTop8 ? "top8" : v == kAnyK ? "anyK" : v == kTop8Rows ? "top8-rows" :
-                         v == kAnyKRows ? "anyK-rows" : "dense",
-                         qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16", nt,
-                         wt ? "write-through" : "write-back", static_cast<long long>(grid));
+                         variant_name(v), out_name(qm), nt, store_name(st),
+                         static_cast<long long>(grid));
         void* args[] = {&p.perm_idx, &p.topk_w, &p.shared_out, &p.residual, &p.gamma,
                         &p.expert_out, &p.V, &p.K, &p};
         const hipError_t e =
@@ -1004,26 +1169,35 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     }
     const int vpt = choose_vpt(path, p.V);
     const int nt = threads_for(p.V, vpt);
-    const void* kern = kernel_for(vpt, v, wt, qm);
+    const void* kern = kernel_for(vpt, v, st, qm);
     const int64_t per = tokens_per_dispatch(nt);
+    // Workgroups per CU, capped through reserved LDS: the tuning override,
+    // else the automatic cap of the 3-vector bf16 stream kernel at large T.
+    int cap = t_force_residency;
+    if (cap == 0 && path == MFR_PATH_STREAM && vpt == 3 && qm == mfr::kOutBf16 && v != kDense &&
+        T >= kCapMinT && H > kCapMinH)
+        cap = kCapPerCu;
+    const size_t lds = lds_for_residency(kern, nt, cap);
+    // tuning only: the per-XCD token ranges
+    const bool xcd_ranges = t_force_order == MFR_ORDER_XCD_RANGES;
     if (g_env_log)
         std::fprintf(stderr,
                      "moe_finalize_rmsnorm: T=%lld H=%lld K=%d variant=%s out=%s path=%s vpt=%d "
-                     "threads=%d stores=%s dispatches=%lld\n",
-                     static_cast<long long>(T), static_cast<long long>(H), p.K,
-                     v == kTop8 ? "top8" : v == kAnyK ? "anyK" : v == kTop8Rows ? "top8-rows" :
-                     v == kAnyKRows ? "anyK-rows" : "dense",
-                     qm == mfr::kOutFp8 ? "fp8" : qm == mfr::kOutBoth ? "bf16+fp8" : "bf16",
-                     path == MFR_PATH_TOKEN ? "token" : "stream", vpt, nt,
-                     wt ? "write-through" : "write-back", static_cast<long long>((T + per - 1) / per));
+                     "threads=%d stores=%s dispatches=%lld reserved_lds=%zu order=%s\n",
+                     static_cast<long long>(T), static_cast<long long>(H), p.K, variant_name(v),
+                     out_name(qm), path == MFR_PATH_TOKEN ? "token" : "stream", vpt, nt,
+                     store_name(st), static_cast<long long>((T + per - 1) / per), lds,
+                     xcd_ranges ? "xcd-ranges" : "default");
     for (int64_t t0 = 0; t0 < T; t0 += per) {
         const int64_t n = T - t0 < per ? T - t0 : per;
         mfr::Params q = t0 == 0 ? p : from_token(p, t0);
         q.T = n;
+        uint32_t vk = static_cast<uint32_t>(q.V) | static_cast<uint32_t>(q.K) << 16;
+        uint32_t xcd_grid = xcd_ranges ? static_cast<uint32_t>(n) : 0u;
         void* args[] = {&q.perm_idx, &q.topk_w, &q.shared_out, &q.residual, &q.gamma,
-                        &q.expert_out, &q.V, &q.K, &q};
+                        &q.expert_out, &vk, &xcd_grid, &q};
         const hipError_t e =
-            hipLaunchKernel(kern, dim3(static_cast<uint32_t>(n)), dim3(nt), args, 0, stream);
+            hipLaunchKernel(kern, dim3(static_cast<uint32_t>(n)), dim3(nt), args, lds, stream);
         if (e != hipSuccess) return MFR_ERR_HIP;
     }
     return MFR_OK;
@@ -1310,7 +1484,7 @@ const char* moe_finalize_rmsnorm_strerror(int status) {
 int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy) {
     if (path < 0 || path > MFR_PATH_PERSIST) return MFR_ERR_ARG;
     if (vectors_per_thread < 0 || vectors_per_thread > kVptMax) return MFR_ERR_ARG;
-    if (store_policy < 0 || store_policy > MFR_STORE_WRITE_THROUGH) return MFR_ERR_ARG;
+    if (store_policy < 0 || store_policy > MFR_STORE_NONTEMPORAL_WRITE_THROUGH) return MFR_ERR_ARG;
     t_force_path = path;
     t_force_vpt = vectors_per_thread;
     t_force_store = store_policy;
@@ -1320,6 +1494,12 @@ int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy) 
 int mfr_tuning_force_residency(int workgroups_per_cu) {
     if (workgroups_per_cu < 0) return MFR_ERR_ARG;
     t_force_residency = workgroups_per_cu;
+    return MFR_OK;
+}
+
+int mfr_tuning_force_token_order(int order) {
+    if (order != MFR_ORDER_DEFAULT && order != MFR_ORDER_XCD_RANGES) return MFR_ERR_ARG;
+    t_force_order = order;
     return MFR_OK;
 }
 

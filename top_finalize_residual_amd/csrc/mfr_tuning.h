@@ -17,10 +17,26 @@
 extern "C" {
 #endif
 
+/* Cache policy of the output stores. AUTO writes back outputs that fit in
+ * the L2 and writes larger ones through (sc1). The two non-temporal
+ * encodings (nt, and nt with sc1) exist for the fused op with exactly eight
+ * slots and bf16 output, on the grid paths; any other launch takes the
+ * automatic policy instead. */
 enum mfr_store_policy {
     MFR_STORE_AUTO = 0,
     MFR_STORE_WRITE_BACK = 1,
-    MFR_STORE_WRITE_THROUGH = 2
+    MFR_STORE_WRITE_THROUGH = 2,
+    MFR_STORE_NONTEMPORAL = 3,
+    MFR_STORE_NONTEMPORAL_WRITE_THROUGH = 4
+};
+
+/* Which token each workgroup of a grid path takes. The hardware hands the
+ * workgroups of a dispatch to the eight XCDs in turn, so with the default
+ * order neighbouring tokens run on different XCDs; XCD_RANGES gives each
+ * XCD one contiguous range of tokens instead. Results are identical. */
+enum mfr_token_order {
+    MFR_ORDER_DEFAULT = 0,
+    MFR_ORDER_XCD_RANGES = 1
 };
 
 /* path: 0 = automatic, else an mfr_path value (MFR_PATH_TOKEN,
@@ -37,11 +53,21 @@ enum mfr_store_policy {
  * sum-of-squares reduction trees differ. */
 int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy);
 
-/* Workgroups per CU of the persistent path's grid, for the calling thread:
- * 0 = as many as fit at once (the default), else at most that many. The grid
- * is that times the CU count, and never more than T. Returns MFR_ERR_ARG for
- * a negative value, else MFR_OK. */
+/* Workgroups per CU, for the calling thread: 0 = automatic, else at most
+ * that many. On the persistent path the grid is that times the CU count
+ * (automatic: as many as fit at once), and never more than T. On the grid
+ * paths the launch reserves enough dynamic LDS that no more than that many
+ * workgroups fit on a CU; where the kernel's registers already allow no
+ * more, or the cap cannot be expressed in LDS, the launch is unchanged, so a
+ * large value means no cap. Automatic there: 2 for the stream path's
+ * 3-vector kernel with bf16 output at H above 5120 from T = 2048 on, else no
+ * cap. Returns
+ * MFR_ERR_ARG for a negative value, else MFR_OK. */
 int mfr_tuning_force_residency(int workgroups_per_cu);
+
+/* Token order of the grid paths for the calling thread: an mfr_token_order
+ * value. Returns MFR_ERR_ARG for other values, else MFR_OK. */
+int mfr_tuning_force_token_order(int order);
 
 #ifdef __cplusplus
 }
