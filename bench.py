@@ -34,6 +34,8 @@ Modes used with rocprofv3 (see profiles/):
   --persist-counters-run  the automatic and the persistent launch at T = 512,
                      2048 and 8192, then the copy probe, for counters
   --state-run        eager launches of the input states, for counters
+  --cold-table       µs per call against T = 1..8192 (fused, FP8-output and
+                     dense calls), fresh inputs on every call
   --summarize-trace  per-(kernel, grid) durations from a kernel_trace.csv
   --summarize-phases durations or counters of a phase run (shape sweep,
                      persistent counters, input states) by dispatch order
@@ -790,30 +792,34 @@ def _shape_list():
     return shapes
 
 
-def _sweep_workloads(ts, cold_bytes, states=False, H=6144):
+def _sweep_workloads(ts, cold_bytes, states=False, H=6144, mode="bf16"):
     """(label, T, nbytes, calls, calls per set and graph, flushed) of each
     workload of a sweep at H (6144: the named workloads), K = 8. HBM-cold:
     one call on each of n
     buffer sets together above cold_bytes (more than twice the Infinity
     Cache); at T = 8192 one set (1.21 GB, cold by size) called 10 times in a
-    row. With states, at T = 8192 also one input set with two output sets
-    alternated, and one set with the Infinity Cache flushed before every
-    call (flushed: each call timed alone, see _sweep)."""
+    row. With states, at T = 8192 also one set with the Infinity Cache
+    flushed before every call (flushed: each call timed alone, see _sweep)
+    and, for the bf16 fused op, one input set with two output sets
+    alternated. mode: the call (stacked_calls)."""
     import synth
     for T in ts:
         cfg = None if H != 6144 else "prefill" if T == 8192 else "batch512" if T == 512 else None
         d = synth.config_inputs(cfg, T) if cfg else synth.generate(
             T, H, 8, scale=2.5, weights="top8_of_256",
             seed=synth.BASE_SEED + 9000 + T + (0 if H == 6144 else H))
-        nb = synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"])
+        nb = (synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"]) if mode == "bf16" else
+              synth.fp8_algorithmic_bytes(d["perm_idx"], d["H"], d["K"]) if mode == "fp8" else
+              synth.dense_algorithmic_bytes(T, d["H"]))
         n = 1 if T == 8192 else max(2, -(-cold_bytes // nb))
-        calls = stacked_calls(d, n, "bf16")
+        calls = stacked_calls(d, n, mode)
         yield str(T), T, nb, calls, 10 if n == 1 else 1, False
         if states and T == 8192:
             yield "8192, cache flushed", T, nb, calls, 5, True
-            del calls
-            calls = mixed_calls(d, 1, 2)
-            yield "8192, 2 output sets", T, nb, calls, 5, False
+            if mode == "bf16":
+                del calls
+                calls = mixed_calls(d, 1, 2)
+                yield "8192, 2 output sets", T, nb, calls, 5, False
         del calls
 
 
@@ -890,14 +896,16 @@ def sweep_shapes(reps=3, cold_bytes=600_000_000, phases=None, ts=SWEEP_TS):
     return {"kind": "shapes", "H": 6144, "K": 8, "unit": "us", "reps": reps, "T": res}
 
 
-def sweep_alternatives(reps=5, cold_bytes=600_000_000, phases=None, ts=ALT_TS, H=6144):
+def sweep_alternatives(reps=5, cold_bytes=600_000_000, phases=None, ts=ALT_TS, H=6144,
+                       mode="bf16"):
     """The alternatives to the shipped launch (ALTERNATIVES) in the same
     harness, at T = 512..8192, and at T = 8192 also with the Infinity Cache
     flushed before every call and with two output sets alternated (the
     outputs then never meet their own lines in the Infinity Cache)."""
-    res = _sweep(_sweep_workloads(ts, cold_bytes, states=True, H=H), list(ALTERNATIVES), reps,
-                 phases, H=H)
-    return {"kind": "alternatives", "H": H, "K": 8, "unit": "us", "reps": reps, "T": res}
+    res = _sweep(_sweep_workloads(ts, cold_bytes, states=True, H=H, mode=mode),
+                 list(ALTERNATIVES), reps, phases, H=H)
+    return {"kind": "alternatives", "mode": mode, "H": H, "K": 8, "unit": "us", "reps": reps,
+            "T": res}
 
 
 def run_sweep(args):
@@ -908,7 +916,7 @@ def run_sweep(args):
     ts = tuple(int(x) for x in args.sweep_ts.split(",")) if args.sweep_ts else default_ts
     kw = dict(reps=args.sweep_reps, ts=ts)
     if alt:
-        fn, kw["H"] = sweep_alternatives, args.sweep_h
+        fn, kw["H"], kw["mode"] = sweep_alternatives, args.sweep_h, args.sweep_mode
     else:
         fn = sweep_shapes
     if args.eager:
@@ -917,6 +925,71 @@ def run_sweep(args):
         print(json.dumps({"phases": phases}), flush=True)
         return
     print(json.dumps({"shape_sweep": fn(**kw)}), flush=True)
+
+
+COLD_TS = (1, 4, 16, 28, 64, 128, 256, 257, 384, 512, 513, 768, 1024, 2048, 4096, 8192)
+
+
+def cold_table(ts=COLD_TS, reps=3, cold_bytes=600_000_000):
+    """µs per call against T, automatic launch, H = 6144, K = 8, fresh
+    inputs on every call: a graph of one call on each of n >= 2 buffer sets
+    together above cold_bytes (more than twice the Infinity Cache), after a
+    cache scrub; median of reps. For the fused op, its FP8-output form
+    (codes and scales, no bf16 normed output) and the dense tail."""
+    import torch
+    import synth
+    out = {}
+    for T in ts:
+        cfg = ("decode" if T in synth.CONFIGS["decode"]["Ts"] else "batch512" if T == 512 else
+               "prefill" if T == 8192 else None)
+        d = synth.config_inputs(cfg, T) if cfg else synth.generate(
+            T, 6144, 8, scale=2.5, weights="top8_of_256", seed=synth.BASE_SEED + 9000 + T)
+        row = {}
+        for mode in ("bf16", "fp8", "dense"):
+            nb = (synth.algorithmic_bytes(d["perm_idx"], d["H"], d["K"]) if mode == "bf16" else
+                  synth.fp8_algorithmic_bytes(d["perm_idx"], d["H"], d["K"]) if mode == "fp8"
+                  else synth.dense_algorithmic_bytes(T, d["H"]))
+            n = max(2, -(-cold_bytes // nb))
+            calls = stacked_calls(d, n, mode)
+            ts_ = []
+            for _ in range(reps):
+                scrub_infinity_cache()
+                ts_.append(time_graph(calls, 1, 3) * 1e3)
+            del calls
+            torch.cuda.empty_cache()
+            us = sorted(ts_)[reps // 2]
+            row[mode] = {"us": round(us, 2), "gbs": round(nb / (us * 1e-6) / 1e9, 1), "sets": n}
+        out[str(T)] = row
+        log(f"cold T={T}: " + ", ".join(f"{m} {v['us']}" for m, v in row.items()))
+    return out
+
+
+def cold_table_lines(path):
+    """The cold_table JSON line as a table."""
+    with open(path) as f:
+        ct = next(json.loads(ln)["cold_table"] for ln in f if '"cold_table"' in ln)
+    ts = list(ct)
+    lines = ["µs per call (and TB/s of algorithmic bytes) against T, automatic launch, H = 6144, "
+             "K = 8, fresh inputs on every call: graphs of one call on each of n buffer sets "
+             "together above 600 MB, after a cache scrub, median of 3:", "",
+             "| T | " + " | ".join(ts) + " |", "|---|" + "---|" * len(ts)]
+    for mode, name in (("bf16", "fused, µs"), ("bf16", "fused, TB/s"), ("fp8", "FP8 output, µs"),
+                       ("dense", "dense, µs")):
+        key = "gbs" if "TB/s" in name else "us"
+        cells = [f"{ct[t][mode][key] / 1000:.2f}" if key == "gbs" else f"{ct[t][mode][key]:.2f}"
+                 for t in ts]
+        lines.append(f"| {name} | " + " | ".join(cells) + " |")
+    return lines
+
+
+def summarize_cold(args):
+    lines = [f"# {args.title}", "", "Commands ($REPO is the repository root, $OUT any output "
+             "directory):", "", "```", args.command, "```", ""] + cold_table_lines(
+                 args.summarize_cold) + ["", f"Kernel code hash of the library measured: "
+                                             f"`{kernel_code_hash()}`."]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 # Input states of the bandwidth figures: (name, T, buffer sets cycled, calls
@@ -1431,7 +1504,9 @@ def sweep_table_lines(path):
     alt = sw.get("kind") == "alternatives"
     what, flag = ("alternatives", "--shape-sweep --alternatives") if alt else ("shapes",
                                                                             "--shape-sweep")
-    lines = [f"Event timing of the same {what} at H = {sw['H']}, K = {sw['K']} "
+    call = {"fp8": "the FP8-output call", "dense": "the dense tail"}.get(sw.get("mode"),
+                                                                      "the fused op")
+    lines = [f"Event timing of the same {what} for {call} at H = {sw['H']}, K = {sw['K']} "
              f"(`bench.py {flag}`: graphs of one call per "
              f"buffer set, or of 10 calls on one set at T = 8192 and 5 calls over two output "
              f"sets; with the cache flushed, the median of 5 calls each timed alone after 512 MB "
@@ -1650,8 +1725,15 @@ def main():
     ap.add_argument("--shape-sweep", action="store_true",
                     help="time every launch shape at T = 64..8192 (H=6144, K=8), HBM-cold")
     ap.add_argument("--sweep-reps", type=int, default=3)
+    ap.add_argument("--cold-table", action="store_true",
+                    help="µs per call against T (fused, FP8-output, dense), fresh inputs")
+    ap.add_argument("--summarize-cold", default="",
+                    help="stdout of bench.py --cold-table: write it as a profiles/ table")
     ap.add_argument("--sweep-h", type=int, default=6144,
                     help="with --shape-sweep --alternatives: the hidden size")
+    ap.add_argument("--sweep-mode", default="bf16", choices=("bf16", "fp8", "dense"),
+                    help="with --shape-sweep --alternatives: the fused op, its FP8-output form "
+                         "or the dense tail")
     ap.add_argument("--alternatives", action="store_true",
                     help="with --shape-sweep: the alternatives to the shipped launch (per-CU cap, "
                          "per-XCD token ranges, store encodings, persistent) at T = 512..8192")
@@ -1700,6 +1782,8 @@ def main():
         return summarize_phases(args)
     if args.summarize_sweep:
         return summarize_sweep(args)
+    if args.summarize_cold:
+        return summarize_cold(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the fused op has no cross-GPU step to time here "
@@ -1714,6 +1798,11 @@ def main():
         return run_latency(args)
     if args.shape_sweep:
         return run_sweep(args)
+    if args.cold_table:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({"cold_table": cold_table()}), flush=True)
+        return
     if args.state_run:
         return run_states(args)
     if args.persist_counters_run:

@@ -328,3 +328,25 @@ def test_summarize_phases_maps_dispatches_by_order(tmp_path):
         bench.summarize_phases(argparse.Namespace(phases_json=str(pj), trace_csv=str(trace),
                                                   counter_csv=[], title="t", command="c",
                                                   out=str(out), append_sweep="", append_states=""))
+
+
+def test_sweep_and_cold_tables(tmp_path):
+    """The sweep table marks the fastest entry of each column and names the
+    alternatives and the hidden size; the cold table prints µs and TB/s."""
+    sw = {"shape_sweep": {"kind": "alternatives", "H": 5120, "K": 8, "unit": "us", "reps": 5,
+                          "T": {"2048": {"auto": 45.0, "cap-2-per-CU": 44.0, "auto_path": "stream",
+                                         "bytes": 1},
+                                "8192, 2 output sets": {"auto": 170.0, "cap-2-per-CU": 171.0,
+                                                        "auto_path": "stream", "bytes": 1}}}}
+    p = tmp_path / "sw.json"
+    p.write_text(json.dumps(sw) + "\n")
+    lines = bench.sweep_table_lines(str(p))
+    assert "for the fused op at H = 5120, K = 8" in lines[0] and "--alternatives" in lines[0]
+    assert lines[2] == "| alternative | T = 2048 | T = 8192, 2 output sets |"
+    assert "| auto | 45.00 | **170.00** |" in lines and "| cap-2-per-CU | **44.00** | 171.00 |" in lines
+    ct = {"cold_table": {"28": {m: {"us": 4.5, "gbs": 900.0, "sets": 100}
+                                for m in ("bf16", "fp8", "dense")}}}
+    c = tmp_path / "c.json"
+    c.write_text("log line\n" + json.dumps(ct) + "\n")
+    lines = bench.cold_table_lines(str(c))
+    assert "| fused, µs | 4.50 |" in lines and "| fused, TB/s | 0.90 |" in lines

@@ -774,15 +774,16 @@ constexpr int64_t kTokenPathMaxT = 511;
 // MI355X at H = 6144: write-back wins at T = 512 (12.6 MB of outputs, which
 // the 32 MB of L2 absorbs), write-through from T = 1024 (25 MB) up.
 constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
-// The stream path's 256-thread, 3-vector kernel with bf16 output (3
-// workgroups per CU by its registers) runs with at most kCapPerCu workgroups
-// per CU from kCapMinT tokens on, for H above kCapMinH (up to 6144, where
-// that kernel ends). Measured on MI355X, every alternative interleaved, at
-// H = 6144: 0.3-1.6% faster from T = 2048 to 8192, with one buffer set, with
-// the Infinity Cache flushed before each call and with alternating outputs
-// alike, and level at T = 512 and 1024; at H = 5120 level or mixed (-2% to
-// +1%), so the rule stops above it. At H = 4096 (another kernel, 7 per CU) a
-// cap of 2 was slower.
+// The stream path's 256-thread, 3-vector kernels of the fused op with bf16
+// or FP8 output (3 workgroups per CU by their registers) run with at most
+// kCapPerCu workgroups per CU from kCapMinT tokens on, for H above kCapMinH
+// (up to 6144, where those kernels end). Measured on MI355X, every
+// alternative interleaved, at H = 6144: bf16 0.3-1.6% faster from T = 2048
+// to 8192, with one buffer set, with the Infinity Cache flushed before each
+// call and with alternating outputs alike, and level at T = 512 and 1024;
+// FP8 0.6-0.9% faster from T = 4096, level at 2048. At H = 5120 (bf16) level
+// or mixed (-2% to +1%), so the rule stops above it. At H = 4096 (another
+// kernel, 7 per CU) and for the dense tail (8 per CU) a cap of 2 was slower.
 constexpr int64_t kCapMinT = 2048;
 constexpr int64_t kCapMinH = 5120;
 constexpr int kCapPerCu = 2;
@@ -1172,9 +1173,10 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     const void* kern = kernel_for(vpt, v, st, qm);
     const int64_t per = tokens_per_dispatch(nt);
     // Workgroups per CU, capped through reserved LDS: the tuning override,
-    // else the automatic cap of the 3-vector bf16 stream kernel at large T.
+    // else the automatic cap of the 3-vector bf16 and FP8 stream kernels at
+    // large T.
     int cap = t_force_residency;
-    if (cap == 0 && path == MFR_PATH_STREAM && vpt == 3 && qm == mfr::kOutBf16 && v != kDense &&
+    if (cap == 0 && path == MFR_PATH_STREAM && vpt == 3 && qm != mfr::kOutBoth && v != kDense &&
         T >= kCapMinT && H > kCapMinH)
         cap = kCapPerCu;
     const size_t lds = lds_for_residency(kern, nt, cap);

@@ -60,8 +60,8 @@ int mfr_tuning_force_launch(int path, int vectors_per_thread, int store_policy);
  * workgroups fit on a CU; where the kernel's registers already allow no
  * more, or the cap cannot be expressed in LDS, the launch is unchanged, so a
  * large value means no cap. Automatic there: 2 for the stream path's
- * 3-vector kernel with bf16 output at H above 5120 from T = 2048 on, else no
- * cap. Returns
+ * 3-vector kernels of the fused op with bf16 or FP8 output, at H above 5120
+ * from T = 2048 on; else no cap. Returns
  * MFR_ERR_ARG for a negative value, else MFR_OK. */
 int mfr_tuning_force_residency(int workgroups_per_cu);
 
