@@ -170,10 +170,11 @@ def make_caller(dd, eps, scale):
     args = [dd[k].data_ptr() for k in ("expert_out", "perm_idx", "topk_w", "shared_out",
                                        "residual", "gamma")]
     ro, no = r_out.data_ptr(), n_out.data_ptr()
+    dev = dd["gamma"].get_device()
+    raw_stream = torch._C._cuda_getCurrentRawStream  # the current stream's handle, no object
 
     def call():
-        s = torch.cuda.current_stream().cuda_stream
-        rc = mfr.moe_finalize_rmsnorm_raw(*args, eps, scale, ro, no, T, H, K, s)
+        rc = mfr.moe_finalize_rmsnorm_raw(*args, eps, scale, ro, no, T, H, K, raw_stream(dev))
         if rc != 0:
             raise RuntimeError(mfr.strerror(rc))
     # the closure holds raw addresses: keep every tensor it writes or reads alive
@@ -720,10 +721,11 @@ def _rate(us, nbytes):
 
 def deferred_overhead():
     """Host cost of the torch-facing deferred path at one decode step (T=28):
-    eager calls of fused_add_rmsnorm (the public consumer norm; with plain
-    tensors it runs the op's kernel without the dispatcher), of the same op
-    through torch.ops (the dispatcher, as under torch.compile), and of the raw
-    C call, against the call replayed from a graph."""
+    eager calls of fused_add_rmsnorm (the public consumer norm), of the same
+    op through torch.ops directly (the dispatcher and the op's C++ kernel, as
+    under torch.compile), and of the raw C call through the ctypes binding
+    (pointers taken once, the current stream's handle per call), against the
+    call replayed from a graph."""
     import torch
     import synth
     import top_finalize_residual_amd as mfr

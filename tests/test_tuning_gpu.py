@@ -142,3 +142,48 @@ def test_cap_reserves_lds_only_below_the_kernel_residency():
     assert lds["T600/bf16/cap0"] == 0 and lds["T600/fp8/cap0"] == 0
     assert lds["T2048/bf16/cap0"] == lds["T2048/bf16/cap2"]
     assert lds["T2048/fp8/cap0"] > 0
+
+
+_GRAPH_FIRST = r"""
+import numpy as np, torch, synth
+from tests import gpu_util as gu
+import top_finalize_residual_amd as mfr
+d = synth.generate(2048, 6144, 8, scale=2.5, seed=21)
+dd = gu.to_device(d)
+r, n = torch.empty_like(dd["residual"]), torch.empty_like(dd["residual"])
+args = [dd[k].data_ptr() for k in ("expert_out", "perm_idx", "topk_w", "shared_out", "residual",
+                                   "gamma")]
+
+
+def call():
+    rc = mfr.moe_finalize_rmsnorm_raw(*args, d["eps"], d["scale"], r.data_ptr(), n.data_ptr(),
+                                      2048, 6144, 8, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, rc
+
+
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):  # the process's first launch: the cap is looked up during capture
+    call()
+outs = []
+for i in range(3):
+    r.fill_(0)
+    n.fill_(0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    outs.append((gu.host_u16(r), gu.host_u16(n)))
+r0, n0 = gu.run(dd, d["eps"], d["scale"])
+for rr, nn in outs:
+    assert np.array_equal(rr, r0) and np.array_equal(nn, n0)
+print("graph-first ok", flush=True)
+"""
+
+
+def test_first_capped_launch_inside_a_graph_capture():
+    """A process whose first launch of the capped stream kernel happens
+    during graph capture: the occupancy and attribute queries behind the cap
+    are made inside the capture, and every replay equals the eager call."""
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", _GRAPH_FIRST], cwd=ROOT, env=env,
+                         capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and "graph-first ok" in out.stdout, out.stderr[-3000:]

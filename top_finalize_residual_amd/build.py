@@ -1,4 +1,5 @@
-"""Build the HIP library (libmoe_finalize_rmsnorm.so) in-tree for gfx950.
+"""Build the HIP library (libmoe_finalize_rmsnorm.so) in-tree for gfx950, and
+the torch operators on top of it (libmfr_torch_ops.so).
 
 The library is compiled with hipcc straight from csrc/ and placed next to
 this file, where the Python binding loads it. Flags:
@@ -18,7 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_finalize_rmsnorm.so")
 PROBE_LIB = os.path.join(PKG, "libmfr_copy_probe.so")
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+OPS_LIB = os.path.join(PKG, "libmfr_torch_ops.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
+CXX = os.environ.get("CXX", "g++")
 
 HIPFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -46,10 +50,39 @@ def _hipcc(sources, out, verbose=False, extra=()):
     return out
 
 
+def _torch_ops(verbose=False):
+    """The torch operators (host C++ against torch's headers and the
+    library above, which it links by its in-tree path)."""
+    import torch
+    from torch.utils import cpp_extension
+    out = OPS_LIB
+    torch_lib = cpp_extension.library_paths()[0]
+    cmd = [CXX, "-std=c++17", "-O2", "-fPIC", "-shared", "-Wall",
+           "-D__HIP_PLATFORM_AMD__", "-DUSE_ROCM",
+           f"-D_GLIBCXX_USE_CXX11_ABI={int(torch._C._GLIBCXX_USE_CXX11_ABI)}",
+           *[f"-I{p}" for p in cpp_extension.include_paths()],
+           "-I", os.path.join(ROCM, "include"), "-I", INCLUDE,
+           "-o", out + ".tmp", os.path.join(CSRC, "mfr_torch_ops.cpp"),
+           f"-L{torch_lib}", "-lc10", "-lc10_hip", "-ltorch_cpu",
+           f"-L{PKG}", "-l:" + os.path.basename(LIB),
+           "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{torch_lib}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building the torch operators failed:\n" + r.stdout + r.stderr)
+    if verbose and (r.stdout + r.stderr).strip():
+        print(r.stdout + r.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose=False):
-    """Compile the product library and the bench's copy-probe library."""
+    """Compile the product library, the bench's copy-probe library and the
+    torch operators."""
     _hipcc([os.path.join(CSRC, "mfr_kernels.hip")], LIB, verbose, extra=PRELOAD)
     _hipcc([os.path.join(CSRC, "copy_probe.hip")], PROBE_LIB, verbose)
+    _torch_ops(verbose)
     return LIB
 
 

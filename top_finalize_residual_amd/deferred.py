@@ -16,10 +16,10 @@ Here:
   * ``fused_add_rmsnorm(hidden, residual, gamma, eps)`` is the consumer norm:
     a deferred MoEOutput goes to the fused finalize kernel, a plain tensor
     (attention / dense MLP output) to the dense residual add + RMSNorm kernel;
-  * both kernels are registered as torch ops that write into caller-provided
-    outputs, so torch sees their effects (torch.compile traces them) and HIP
-    graph capture records them; an eager call with plain tensors runs the
-    op's kernel directly, without the dispatcher's overhead: ``mfr::moe_finalize_rmsnorm`` and ``mfr::residual_add_rmsnorm``
+  * both kernels are registered as torch ops, with C++ kernels, that write
+    into caller-provided outputs, so torch sees their effects (torch.compile
+    traces them) and HIP graph capture records them:
+    ``mfr::moe_finalize_rmsnorm`` and ``mfr::residual_add_rmsnorm``
     write a separate residual_out; ``mfr::moe_finalize_rmsnorm_`` and
     ``mfr::residual_add_rmsnorm_`` update the residual stream in place (it is
     then the one mutated argument, never passed twice); the ``_fp8`` forms of
@@ -27,108 +27,37 @@ Here:
     activation format of an FP8 projection.
 Every step of the arithmetic runs in the HIP library; nothing here computes.
 """
+import os
 from dataclasses import dataclass
 from typing import Optional, Tuple, Union
 
 import torch
 
 from . import binding
+from . import build as _build
 
-_LIB_NS = "mfr"
+# The ops' schemas and kernels are C++ (csrc/mfr_torch_ops.cpp, built next to
+# the HIP library it calls): an eager call through torch.ops then costs the
+# dispatcher and the launch, not a Python layer. The kernels refuse tensors
+# off the GPU.
+if not os.path.exists(_build.OPS_LIB):
+    raise ImportError(f"{_build.OPS_LIB} is not built; run top_finalize_residual_amd/build.py first")
+torch.ops.load_library(_build.OPS_LIB)
 
-# The ops are defined on a torch.library.Library with explicit schemas and a
-# plain kernel per device type: dispatch through torch.ops then costs a few
-# microseconds, where torch.library.custom_op's wrapper layers cost several
-# times that per eager call. Each kernel is the binding call itself; the
-# binding refuses tensors off the GPU.
-_LIB = torch.library.Library(_LIB_NS, "DEF")
-
-_MOE_ARGS = ("Tensor expert_out, Tensor perm_idx, Tensor topk_w, Tensor shared_out, "
-             "{residual}, Tensor gamma, float eps, float scale")
-_DENSE_ARGS = "Tensor x, {residual}, Tensor gamma, float eps"
-
-
-def _moe_op(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, residual_out,
-            normed_out):
-    binding.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
-                                 scale, residual_out=residual_out, normed_out=normed_out)
-
-
-def _moe_op_(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale, normed_out):
-    binding.moe_finalize_rmsnorm(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps,
-                                 scale, residual_out=residual, normed_out=normed_out)
-
-
-def _moe_fp8_op(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
-                residual_out, normed_fp8, fp8_scale):
-    binding.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
-                                     eps, scale, residual_out=residual_out, normed_fp8=normed_fp8,
-                                     fp8_scale=fp8_scale)
-
-
-def _moe_fp8_op_(expert_out, perm_idx, topk_w, shared_out, residual, gamma, eps, scale,
-                 normed_fp8, fp8_scale):
-    binding.moe_finalize_rmsnorm_fp8(expert_out, perm_idx, topk_w, shared_out, residual, gamma,
-                                     eps, scale, residual_out=residual, normed_fp8=normed_fp8,
-                                     fp8_scale=fp8_scale)
-
-
-def _dense_op(x, residual, gamma, eps, residual_out, normed_out):
-    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual_out,
-                                 normed_out=normed_out)
-
-
-def _dense_op_(x, residual, gamma, eps, normed_out):
-    binding.residual_add_rmsnorm(x, residual, gamma, eps, residual_out=residual,
-                                 normed_out=normed_out)
-
-
-def _dense_fp8_op(x, residual, gamma, eps, residual_out, normed_fp8, fp8_scale):
-    binding.residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=residual_out,
-                                     normed_fp8=normed_fp8, fp8_scale=fp8_scale)
-
-
-def _dense_fp8_op_(x, residual, gamma, eps, normed_fp8, fp8_scale):
-    binding.residual_add_rmsnorm_fp8(x, residual, gamma, eps, residual_out=residual,
-                                     normed_fp8=normed_fp8, fp8_scale=fp8_scale)
+_OP_NAMES = ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_", "moe_finalize_rmsnorm_fp8",
+             "moe_finalize_rmsnorm_fp8_", "residual_add_rmsnorm", "residual_add_rmsnorm_",
+             "residual_add_rmsnorm_fp8", "residual_add_rmsnorm_fp8_")
 
 
 def _no_output(*args):
+    """Fake-tensor kernel of every op: they write into their arguments and
+    return nothing."""
     return None
 
 
-# name -> (schema, kernel). Mutated tensors carry alias annotations; the
-# in-place forms (trailing underscore) mutate the residual stream itself.
-_BF16_OUT = "Tensor(b!) normed_out"
-_FP8_OUT = "Tensor(b!) normed_fp8, Tensor(c!) fp8_scale"
-_OPS_DEF = {
-    "moe_finalize_rmsnorm": (
-        _MOE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _BF16_OUT,
-        _moe_op),
-    "moe_finalize_rmsnorm_": (
-        _MOE_ARGS.format(residual="Tensor(a!) residual") + ", " + _BF16_OUT, _moe_op_),
-    "moe_finalize_rmsnorm_fp8": (
-        _MOE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _FP8_OUT,
-        _moe_fp8_op),
-    "moe_finalize_rmsnorm_fp8_": (
-        _MOE_ARGS.format(residual="Tensor(a!) residual") + ", " + _FP8_OUT, _moe_fp8_op_),
-    "residual_add_rmsnorm": (
-        _DENSE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _BF16_OUT,
-        _dense_op),
-    "residual_add_rmsnorm_": (
-        _DENSE_ARGS.format(residual="Tensor(a!) residual") + ", " + _BF16_OUT, _dense_op_),
-    "residual_add_rmsnorm_fp8": (
-        _DENSE_ARGS.format(residual="Tensor residual") + ", Tensor(a!) residual_out, " + _FP8_OUT,
-        _dense_fp8_op),
-    "residual_add_rmsnorm_fp8_": (
-        _DENSE_ARGS.format(residual="Tensor(a!) residual") + ", " + _FP8_OUT, _dense_fp8_op_),
-}
-
-for _name, (_schema, _kernel) in _OPS_DEF.items():
-    _LIB.define(f"{_name}({_schema}) -> ()")
-    _LIB.impl(_name, _kernel, "CUDA")
-    _LIB.impl(_name, _kernel, "CPU")  # the binding refuses CPU tensors with a clear error
-    torch.library.register_fake(f"{_LIB_NS}::{_name}", _no_output, lib=_LIB)
+for _name in _OP_NAMES:
+    torch.library.register_fake(f"mfr::{_name}")(_no_output)
+_OP = {name: getattr(torch.ops.mfr, name).default for name in _OP_NAMES}
 
 
 @dataclass
@@ -213,17 +142,6 @@ _OPS = {
     (False, True, False): "residual_add_rmsnorm_fp8",
     (False, True, True): "residual_add_rmsnorm_fp8_",
 }
-_len_dispatch_stack = torch._C._len_torch_dispatch_stack
-
-
-def _direct(ref: torch.Tensor) -> bool:
-    """Whether an eager call may go straight to the op's kernel: a plain
-    tensor, no torch dispatch mode active (fake tensors, functionalization,
-    tracing) and no torch.compile tracing. The kernel is what the dispatcher
-    would run, so results and effects are the same; only the dispatch cost is
-    saved. Anything else goes through torch.ops."""
-    return type(ref) is torch.Tensor and _len_dispatch_stack() == 0 and \
-        not torch.compiler.is_compiling()
 
 
 def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Tensor,
@@ -267,8 +185,7 @@ def fused_add_rmsnorm(hidden: Union[MoEOutput, torch.Tensor], residual: torch.Te
         args = (rows, idx, w, hidden.shared, residual, gamma, float(eps), scale)
     else:
         args = (hidden, residual, gamma, float(eps))
-    name = _OPS[(moe, fp8, r_out is None)]
-    op = _OPS_DEF[name][1] if _direct(ref) else getattr(torch.ops.mfr, name)
+    op = _OP[_OPS[(moe, fp8, r_out is None)]]
     if r_out is None:
         op(*args, *outs)
         return (residual,) + outs
