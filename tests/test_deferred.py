@@ -78,3 +78,47 @@ def test_cpu_tensors_are_refused():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         mfr.fused_add_rmsnorm(x, torch.zeros_like(x), torch.ones(64, dtype=torch.bfloat16), 1e-6)
+
+
+OP_NAMES = ("moe_finalize_rmsnorm", "moe_finalize_rmsnorm_", "moe_finalize_rmsnorm_fp8",
+            "moe_finalize_rmsnorm_fp8_", "residual_add_rmsnorm", "residual_add_rmsnorm_",
+            "residual_add_rmsnorm_fp8", "residual_add_rmsnorm_fp8_")
+
+
+def test_op_schemas_mark_what_each_op_writes():
+    """The C++ definitions carry the alias annotations that tell torch which
+    arguments each op writes (and that the in-place forms write the residual
+    stream itself); no op returns anything."""
+    written = {
+        "moe_finalize_rmsnorm": ("residual_out", "normed_out"),
+        "moe_finalize_rmsnorm_": ("residual", "normed_out"),
+        "moe_finalize_rmsnorm_fp8": ("residual_out", "normed_fp8", "fp8_scale"),
+        "moe_finalize_rmsnorm_fp8_": ("residual", "normed_fp8", "fp8_scale"),
+        "residual_add_rmsnorm": ("residual_out", "normed_out"),
+        "residual_add_rmsnorm_": ("residual", "normed_out"),
+        "residual_add_rmsnorm_fp8": ("residual_out", "normed_fp8", "fp8_scale"),
+        "residual_add_rmsnorm_fp8_": ("residual", "normed_fp8", "fp8_scale"),
+    }
+    for name in OP_NAMES:
+        schema = getattr(torch.ops.mfr, name).default._schema
+        assert len(schema.returns) == 0, name
+        got = tuple(a.name for a in schema.arguments if a.alias_info is not None and
+                    a.alias_info.is_write)
+        assert got == written[name], (name, got)
+
+
+def test_ops_refuse_cpu_tensors_directly():
+    """Through torch.ops too, CPU tensors get a clear error, not a CPU result."""
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        torch.ops.mfr.residual_add_rmsnorm(x, x.clone(), g, 1e-6, torch.empty_like(x),
+                                           torch.empty_like(x))
+    u = (torch.zeros(32, 64, dtype=torch.bfloat16), torch.zeros(4, 8, dtype=torch.int32),
+         torch.zeros(4, 8))
+    with pytest.raises(ValueError, match="GPU"):
+        torch.ops.mfr.moe_finalize_rmsnorm(*u, x, x.clone(), g, 1e-6, 1.0, torch.empty_like(x),
+                                           torch.empty_like(x))
+    with pytest.raises(TypeError, match="perm_idx"):
+        torch.ops.mfr.moe_finalize_rmsnorm(u[0], u[1].long(), u[2], x, x.clone(), g, 1e-6, 1.0,
+                                           torch.empty_like(x), torch.empty_like(x))
