@@ -241,3 +241,48 @@ def test_fp8_custom_ops_pass_opcheck():
     torch.library.opcheck(torch.ops.mfr.residual_add_rmsnorm_fp8_.default,
                           (dd["shared_out"], dd["residual"].clone(), dd["gamma"], d["eps"], q, s),
                           test_utils=utils)
+
+
+def test_ops_pass_every_opcheck():
+    """All of torch.library.opcheck's default checks (schema, autograd
+    registration, fake tensors, AOT dispatch with dynamic shapes) on the C++
+    operators, out of place and in place."""
+    d = synth.generate(4, 2048, 8, seed=64)
+    dd = gu.to_device(d)
+    ro, no = torch.empty_like(dd["residual"]), torch.empty_like(dd["residual"])
+    T, H = dd["residual"].shape
+    # codes as uint8, as in the FP8 opcheck above: the schema check compares
+    # values with arithmetic torch lacks for float8
+    q = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((T,), dtype=torch.float32, device="cuda")
+    moe = (dd["expert_out"], dd["perm_idx"], dd["topk_w"], dd["shared_out"])
+    cases = [
+        ("moe_finalize_rmsnorm", (*moe, dd["residual"], dd["gamma"], d["eps"], d["scale"], ro, no)),
+        ("moe_finalize_rmsnorm_", (*moe, dd["residual"].clone(), dd["gamma"], d["eps"], d["scale"],
+                                   no)),
+        ("moe_finalize_rmsnorm_fp8", (*moe, dd["residual"], dd["gamma"], d["eps"], d["scale"], ro,
+                                      q, sc)),
+        ("residual_add_rmsnorm", (dd["shared_out"], dd["residual"], dd["gamma"], d["eps"], ro, no)),
+        ("residual_add_rmsnorm_fp8_", (dd["shared_out"], dd["residual"].clone(), dd["gamma"],
+                                       d["eps"], q, sc)),
+    ]
+    for name, args in cases:
+        torch.library.opcheck(getattr(torch.ops.mfr, name).default, args)
+
+
+def test_ops_empty_call_and_library_errors():
+    """Through torch.ops: T = 0 enqueues nothing and succeeds; an output that
+    overlaps an input is refused by the library, whose status text the
+    error carries."""
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    torch.ops.mfr.residual_add_rmsnorm(x, x.clone(), g, 1e-6, x.clone(), x.clone())
+    torch.ops.mfr.moe_finalize_rmsnorm(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"),
+                                       torch.zeros((0, 8), dtype=torch.int32, device="cuda"),
+                                       torch.zeros((0, 8), device="cuda"), x, x.clone(), g, 1e-6,
+                                       1.0, x.clone(), x.clone())
+    torch.cuda.synchronize()
+    a = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros_like(a)
+    with pytest.raises(RuntimeError, match="overlaps"):
+        torch.ops.mfr.residual_add_rmsnorm(a, r, g, 1e-6, a, torch.empty_like(a))

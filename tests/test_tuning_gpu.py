@@ -187,3 +187,21 @@ def test_first_capped_launch_inside_a_graph_capture():
     out = subprocess.run([sys.executable, "-c", _GRAPH_FIRST], cwd=ROOT, env=env,
                          capture_output=True, text=True, timeout=300)
     assert out.returncode == 0 and "graph-first ok" in out.stdout, out.stderr[-3000:]
+
+
+@pytest.mark.parametrize("T,H", [(2048, 6144), (2049, 5128), (3001, 5632)],
+                         ids=["T2048-H6144", "T2049-H5128", "T3001-H5632"])
+def test_capped_shapes_against_the_oracle(T, H):
+    """Shapes the automatic per-CU cap applies to (the 3-vector stream kernel
+    above H = 5120 from T = 2048), with bf16 and with FP8-only output, every
+    token against the oracle."""
+    from tests.test_fp8_gpu import check_fp8
+    d = synth.generate(T, H, 8, scale=2.5, mask_frac=0.03, seed=synth.BASE_SEED + 7300 + T + H,
+                       extra_rows=2)
+    dd = gu.to_device(d)
+    r, n = gu.run(dd, d["eps"], d["scale"])
+    gu.check_all_tokens(d, r, n)
+    rq, q, sc, _ = run_fp8(dd, d)
+    assert np.array_equal(rq, r)
+    for t0, t1, ref in gu.oracle_chunks(T, gu.finalize_evaluator(d)):
+        check_fp8(q[t0:t1], sc[t0:t1], ref, d["gamma"], d["eps"])
