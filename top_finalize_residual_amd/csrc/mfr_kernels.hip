@@ -1014,10 +1014,10 @@ int cu_count() {
 }
 
 // Workgroups of nt threads of one kernel that fit on a CU at once (from the
-// kernel's register and LDS use), queried once per (kernel, nt).
+// kernel's register and LDS use), queried once per (kernel, nt, device).
 struct Residency {
     const void* kern;
-    int nt;
+    int nt, dev;
     int per_cu;
 };
 std::mutex g_res_mu;
@@ -1025,13 +1025,16 @@ Residency g_res[512];
 int g_res_n = 0;
 
 int resident_per_cu(const void* kern, int nt) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     std::lock_guard<std::mutex> lock(g_res_mu);
     for (int i = 0; i < g_res_n; ++i)
-        if (g_res[i].kern == kern && g_res[i].nt == nt) return g_res[i].per_cu;
+        if (g_res[i].kern == kern && g_res[i].nt == nt && g_res[i].dev == dev)
+            return g_res[i].per_cu;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, nt, 0) != hipSuccess || n <= 0)
         return 1;
-    if (g_res_n < 512) g_res[g_res_n++] = {kern, nt, n};
+    if (g_res_n < 512) g_res[g_res_n++] = {kern, nt, dev, n};
     return n;
 }
 
