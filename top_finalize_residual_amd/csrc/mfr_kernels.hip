@@ -781,8 +781,8 @@ constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
 // alternative interleaved, at H = 6144: bf16 0.3-1.6% faster from T = 2048
 // to 8192, with one buffer set, with the Infinity Cache flushed before each
 // call and with alternating outputs alike, and level at T = 512 and 1024;
-// FP8 0.6-0.9% faster from T = 4096, level at 2048. At H = 5120 (bf16) level
-// or mixed (-2% to +1%), so the rule stops above it. At H = 4096 (another
+// FP8 0.7-0.9% faster at T = 8192 in two sweeps, level at 2048 and 4096. At
+// H = 5120 (bf16) level or mixed (-2% to +1%), so the rule stops above it. At H = 4096 (another
 // kernel, 7 per CU) and for the dense tail (8 per CU) a cap of 2 was slower.
 constexpr int64_t kCapMinT = 2048;
 constexpr int64_t kCapMinH = 5120;
