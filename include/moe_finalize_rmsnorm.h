@@ -119,7 +119,8 @@ enum mfr_path {
     MFR_PATH_STREAM = 2,  /* large T, bandwidth: 256 threads per token, write-through stores once
                              the outputs outgrow the L2 */
     MFR_PATH_PERSIST = 3  /* large T, bandwidth: persistent multi-token workgroups, two tokens in
-                             flight each (H <= 6144, K <= 8) */
+                             flight each (H <= 6144, K <= 8; not the checked calls with FP8
+                             output, which take the automatic path) */
 };
 
 /* The fused op. Definition, layouts, limits and errors: see above. */

@@ -225,3 +225,18 @@ def test_extreme_rows():
     d = extreme_inputs(seed=5600, exps=EXPS * 40)
     r, n = gu.run(gu.to_device(d), d["eps"], d["scale"], path=P, residency=1)
     check_rows(d, r, n)
+
+
+def test_checked_fp8_calls_take_the_automatic_path():
+    """The persistent kernel does not serve the checked entry points with FP8
+    output: forced onto it, those calls run the automatic path, bit for bit
+    the same as with no override."""
+    T, H, K = 700, 6144, 8
+    d = synth.generate(T, H, K, scale=2.5, seed=5700)
+    dd = gu.to_device(d)
+    with tuning.forced(P):
+        forced = run_fp8(dd, d, bf16_normed=True, api="binding")
+    auto = run_fp8(dd, d, bf16_normed=True, api="binding")
+    for a, b in zip(forced, auto):
+        assert np.array_equal(a, b)
+    check_fp8(forced[1], forced[2], gu.oracle_for(d), d["gamma"], d["eps"])

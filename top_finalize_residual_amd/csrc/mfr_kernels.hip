@@ -974,13 +974,24 @@ const void* pick_persist_store(bool wt) {
               : reinterpret_cast<const void*>(&mfr::mfr_persist_kernel<KT, mfr::kAuxOut, QM, ROWS>);
 }
 
+// The persistent kernel serves every call except the checked ones with FP8
+// output: those need more registers than its 768-thread workgroups leave
+// (they spilled), so they take the automatic path instead.
+bool persist_serves(Variant v, int qm) {
+    return qm == mfr::kOutBf16 || (v != kTop8Rows && v != kAnyKRows);
+}
+
 template <int QM>
 const void* pick_persist_variant(Variant v, bool wt) {
     switch (v) {
         case kTop8: return pick_persist_store<8, QM>(wt);
         case kAnyK: return pick_persist_store<0, QM>(wt);
-        case kTop8Rows: return pick_persist_store<8, QM, true>(wt);
-        case kAnyKRows: return pick_persist_store<0, QM, true>(wt);
+        case kTop8Rows:
+            if constexpr (QM == mfr::kOutBf16) return pick_persist_store<8, QM, true>(wt);
+            return nullptr;  // not served (persist_serves)
+        case kAnyKRows:
+            if constexpr (QM == mfr::kOutBf16) return pick_persist_store<0, QM, true>(wt);
+            return nullptr;  // not served (persist_serves)
         default: return pick_persist_store<-1, QM>(wt);
     }
 }
@@ -1146,7 +1157,9 @@ int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t 
     p.T = T;
     p.h_f = static_cast<float>(H);
     p.V = static_cast<int>(H / 8);
-    const int path = choose_path(T, H, v == kDense ? 1 : p.K);
+    int path = choose_path(T, H, v == kDense ? 1 : p.K);
+    if (path == MFR_PATH_PERSIST && !persist_serves(v, qm))
+        path = T <= kTokenPathMaxT ? MFR_PATH_TOKEN : MFR_PATH_STREAM;
     const int st = store_policy(path, T, H, v, qm);
     const bool wt = st == kStoreWt;
     if (path == MFR_PATH_PERSIST) {
