@@ -117,7 +117,7 @@ enum mfr_path {
     MFR_PATH_UNSUPPORTED = 0,
     MFR_PATH_TOKEN = 1,   /* small T, latency: widest workgroup per token (768 threads at H = 6144) */
     MFR_PATH_STREAM = 2,  /* large T, bandwidth: 256 threads per token, write-through stores once
-                             the outputs outgrow the L2 */
+                             the outputs pass 12 MiB */
     MFR_PATH_PERSIST = 3  /* large T, bandwidth: persistent multi-token workgroups, two tokens in
                              flight each (H <= 6144, K <= 8; not the checked calls with FP8
                              output, which take the automatic path) */

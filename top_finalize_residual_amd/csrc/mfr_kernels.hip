@@ -770,10 +770,13 @@ constexpr uint32_t kNoRowBound = 0x80000000u;
 // 448 and level with it at 511 and 512; from T = 768 the stream shape is
 // ahead.
 constexpr int64_t kTokenPathMaxT = 511;
-// Output bytes (both outputs) from which the stores write through. Measured on
-// MI355X at H = 6144: write-back wins at T = 512 (12.6 MB of outputs, which
-// the 32 MB of L2 absorbs), write-through from T = 1024 (25 MB) up.
-constexpr uint64_t kWriteThroughMinBytes = 16ull << 20;
+// Output bytes (both outputs) above which the stores write through. Measured
+// on MI355X at H = 6144 in three sweeps: write-back wins at T = 512 (12 MiB of
+// outputs, which the 32 MB of L2 absorbs, every CU finishing its two tokens
+// together), write-through from T = 513 up (3-5% at 513, 2-3% at 640, level at
+// 768, 3-5% from 2048), where the grid's last tokens run alone and written-
+// back outputs would wait in the L2 for the end of the kernel.
+constexpr uint64_t kWriteThroughAboveBytes = 12ull << 20;
 // The stream path's 256-thread, 3-vector kernels of the fused op with bf16
 // or FP8 output (3 workgroups per CU by their registers) run with at most
 // kCapPerCu workgroups per CU from kCapMinT tokens on, for H above kCapMinH
@@ -908,7 +911,7 @@ int store_policy(int path, int64_t T, int64_t H, Variant v, int qm) {
     if ((f == MFR_STORE_NONTEMPORAL || f == MFR_STORE_NONTEMPORAL_WRITE_THROUGH) && v == kTop8 &&
         qm == mfr::kOutBf16 && path != MFR_PATH_PERSIST)
         return f == MFR_STORE_NONTEMPORAL ? kStoreNt : kStoreNtWt;
-    return path != MFR_PATH_TOKEN && static_cast<uint64_t>(T) * H * 4 >= kWriteThroughMinBytes
+    return path != MFR_PATH_TOKEN && static_cast<uint64_t>(T) * H * 4 > kWriteThroughAboveBytes
                ? kStoreWt
                : kStoreWb;
 }
