@@ -765,10 +765,10 @@ constexpr int kVptMax = 4;
 constexpr uint32_t kNoRowBound = 0x80000000u;
 // Token counts up to this use the token path (widest workgroup per token),
 // that is below two tokens per CU on the 256 CUs of an MI355X. Measured there
-// at H = 6144 (HBM-cold, every shape interleaved, median of 5): the widest
-// workgroup is 1-4% faster than the 256-thread stream shape from T = 257 to
-// 448 and level with it at 511 and 512; from T = 768 the stream shape is
-// ahead.
+// at H = 6144 (HBM-cold, every shape interleaved): the widest workgroup is
+// 1-2.6% faster than the 256-thread stream shape from T = 257 to 368 and
+// level with it, within the run-to-run spread, from 384 to 512; from T = 640
+// the stream shape is ahead.
 constexpr int64_t kTokenPathMaxT = 511;
 // Output bytes (both outputs) above which the stores write through. Measured
 // on MI355X at H = 6144 in three sweeps: write-back wins at T = 512 (12 MiB of
