@@ -240,6 +240,11 @@ def _probe_lib():
                                     ctypes.c_void_p]
     lib.mfr_empty_probe.restype = ctypes.c_int
     lib.mfr_empty_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mfr_mix_probe.restype = ctypes.c_int
+    lib.mfr_mix_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                  ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
     return lib
 
 
@@ -279,6 +284,168 @@ def probe_ceilings(nbytes=1 << 30, reps=10):
     del src, dst, sink
     torch.cuda.empty_cache()
     return best["copy"], best["read"], best["write"]
+
+
+# The mixed-stream probe at the headline chunk's bytes: its reads (rows,
+# shared and residual) against its writes with bf16 output, or with FP8 codes
+# (residual_out plus one byte per element). Per thread and unit of work: 30
+# vectors read for 6 written is one token at 256 threads with bf16 output;
+# 20 for 3 the FP8 proportion.
+MIX_PAIRS = {"bf16": (30, 6), "fp8": (20, 3)}
+MIX_READ_BYTES = 8192 * 8 * 6144 * 2 + 2 * 8192 * 6144 * 2  # rows, shared, residual
+MIX_WRITE_BYTES = {"bf16": 2 * 8192 * 6144 * 2, "fp8": 8192 * 6144 * 3}
+MIX_WT, MIX_PIPE = 1, 2  # mfr_mix_probe flags
+
+
+class _MixProbe:
+    """The mixed-stream probe on one pair of buffers of the chunk's sizes."""
+
+    def __init__(self):
+        import torch
+        self.lib = _probe_lib()
+        self.src = torch.empty(MIX_READ_BYTES, dtype=torch.uint8, device="cuda")
+        self.dst = torch.empty(MIX_WRITE_BYTES["bf16"], dtype=torch.uint8, device="cuda")
+        self.src.fill_(1)
+        self.cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def gbs_us(self, reads, writes, flags, grid, per_cu, reps=10):
+        """(GB/s of read + write bytes, µs per call), or None where the
+        residency cannot be set that way."""
+        import ctypes
+        import torch
+        rb, wb = ctypes.c_int64(0), ctypes.c_int64(0)
+        wbytes = MIX_WRITE_BYTES["fp8" if reads * 3 == writes * 20 else "bf16"]
+        rc = []
+
+        def call():
+            r = self.lib.mfr_mix_probe(self.src.data_ptr(), MIX_READ_BYTES, self.dst.data_ptr(),
+                                       wbytes, reads, writes, flags, grid, per_cu, ctypes.byref(rb),
+                                       ctypes.byref(wb), torch.cuda.current_stream().cuda_stream)
+            if r == 3:
+                rc.append(r)
+                return
+            if r != 0:
+                raise RuntimeError(f"mix probe failed ({r})")
+        call()
+        torch.cuda.synchronize()
+        if rc:
+            return None
+        ms = time_calls([call], reps, 2)
+        return (rb.value + wb.value) / (ms * 1e-3) / 1e9, ms * 1e3
+
+    def close(self):
+        import torch
+        del self.src, self.dst
+        torch.cuda.empty_cache()
+
+
+def mix_probe_ceilings(reps=10):
+    """GB/s (read + write bytes) of the mixed-stream probe at the headline
+    chunk's own byte counts, with bf16 output and with FP8 codes, in the
+    headline's cache state (one buffer set, calls back to back). Best over
+    write-back and write-through stores and four launch shapes: one workgroup
+    per unit of work (as the fused op launches one per token), the same capped
+    at 2 workgroups per CU through reserved LDS (as the fused op at this
+    size), and grids of 2 and 8 workgroups per CU that walk the units; every
+    combination is returned too, as {name: [GB/s, µs]}."""
+    probe = _MixProbe()
+    cus = probe.cus
+    out = {}
+    for mode, (a, b) in MIX_PAIRS.items():
+        best, detail = 0.0, {}
+        for wt in (0, MIX_WT):
+            for grid, per_cu, shape in ((0, 0, "per-unit"), (0, 2, "per-unit-cap2"),
+                                        (2 * cus, 0, "2-per-cu"), (8 * cus, 0, "8-per-cu")):
+                r = probe.gbs_us(a, b, wt, grid, per_cu, reps)
+                if r is None:
+                    continue
+                detail[f"{'wt' if wt else 'wb'}-{shape}"] = [round(r[0], 1), round(r[1], 2)]
+                best = max(best, r[0])
+        out[mode] = {"gbs": round(best, 1), "shapes": detail}
+    probe.close()
+    return out
+
+
+# The depth sweep: vectors in flight per thread (reads of one unit, with a
+# fifth as many writes) against workgroups per CU, for the one-unit-per-
+# workgroup form (capped through reserved LDS) and the pipelined form (a
+# grid of that many workgroups per CU walking the units).
+MIX_DEPTHS = (10, 15, 20, 25, 30, 40)
+MIX_CAPS = (1, 2, 3, 4)
+
+
+def mix_sweep(reps=3):
+    """Median GB/s over reps interleaved repetitions of every depth x
+    residency of the mixed-stream probe (bf16 proportion, write-through
+    stores), the one-unit form with no cap, and the FP8 proportion at its
+    two depths; keys "unit/A<reads>/cap<n>", "pipe/A<reads>/<n>-per-cu",
+    "unit/A<reads>/nocap" and "fp8/A<reads>/cap<n>"."""
+    import statistics
+    probe = _MixProbe()
+    runs = {}
+    for rep in range(reps):
+        for a in MIX_DEPTHS:
+            for n in MIX_CAPS:
+                r = probe.gbs_us(a, a // 5, MIX_WT, 0, n)
+                if r is not None:
+                    runs.setdefault(f"unit/A{a}/cap{n}", []).append(r[0])
+                r = probe.gbs_us(a, a // 5, MIX_WT | MIX_PIPE, n * probe.cus, 0)
+                if r is not None:
+                    runs.setdefault(f"pipe/A{a}/{n}-per-cu", []).append(r[0])
+            r = probe.gbs_us(a, a // 5, MIX_WT, 0, 0)
+            runs.setdefault(f"unit/A{a}/nocap", []).append(r[0])
+        for a, b in ((20, 3), (40, 6)):
+            for n in (1, 2, 3):
+                r = probe.gbs_us(a, b, MIX_WT, 0, n)
+                if r is not None:
+                    runs.setdefault(f"fp8/A{a}/cap{n}", []).append(r[0])
+        log(f"mix sweep: repetition {rep + 1} of {reps}")
+    probe.close()
+    return {k: round(statistics.median(v), 1) for k, v in runs.items()}
+
+
+def mix_sweep_lines(path):
+    """Markdown tables of a mix_sweep record."""
+    with open(path) as f:
+        rec = json.load(f)
+    lines = ["GB/s (read + write bytes) of the mixed-stream probe (`csrc/copy_probe.hip`) over "
+             "the 8192-token chunk's bytes (1.007 GB read; 201 MB written with bf16 output, "
+             "151 MB with FP8 codes), one buffer set, calls back to back, write-through stores, "
+             "median of the interleaved repetitions. A unit is one workgroup's share: A "
+             "16-byte vectors read per thread, all in flight at once, then A/5 written (A = 30 "
+             "is one token of the fused op with bf16 output at 256 threads). The in-flight "
+             "bytes per CU are the workgroups per CU times A x 4 KiB.", "",
+             "One unit per workgroup (the fused op's launch), at most n workgroups per CU "
+             "(reserved LDS; a dash where the registers allow fewer), and with no cap:", "",
+             "| A (KiB per unit) | n = 1 | n = 2 | n = 3 | n = 4 | no cap |",
+             "|---|---|---|---|---|---|"]
+    for a in MIX_DEPTHS:
+        row = [rec.get(f"unit/A{a}/cap{n}") for n in MIX_CAPS] + [rec.get(f"unit/A{a}/nocap")]
+        lines.append(f"| {a} ({a * 4}) | " + " | ".join("—" if v is None else f"{v:,.0f}"
+                                                         for v in row) + " |")
+    lines += ["", "Pipelined (each workgroup walks its units and issues the next unit's loads "
+              "before the current unit's stores, as the persistent multi-token kernel does), a "
+              "grid of n workgroups per CU:", "",
+              "| A (KiB per unit) | n = 1 | n = 2 | n = 3 | n = 4 |", "|---|---|---|---|---|"]
+    for a in MIX_DEPTHS:
+        row = [rec.get(f"pipe/A{a}/{n}-per-cu") for n in MIX_CAPS]
+        lines.append(f"| {a} ({a * 4}) | " + " | ".join("—" if v is None else f"{v:,.0f}"
+                                                         for v in row) + " |")
+    lines += ["", "FP8 proportion (A read for 3A/20 written), one unit per workgroup:", "",
+              "| A (KiB per unit) | n = 1 | n = 2 | n = 3 |", "|---|---|---|---|"]
+    for a in (20, 40):
+        row = [rec.get(f"fp8/A{a}/cap{n}") for n in (1, 2, 3)]
+        lines.append(f"| {a} ({a * 4}) | " + " | ".join("—" if v is None else f"{v:,.0f}"
+                                                         for v in row) + " |")
+    return lines
+
+
+def summarize_mix(args):
+    lines = [f"# {args.title}", "", "Commands ($REPO is the repository root, $OUT any output "
+             "directory):", "", "```", args.command, "```", ""] + mix_sweep_lines(args.summarize_mix)
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def launch_floor_us(grid=1, threads=64):
@@ -1233,6 +1400,12 @@ def run_bench(args):
         cp, rd, wr = probe_ceilings()
         rec["probe_ceilings_gbs"] = {"copy": round(cp, 1), "read_only": round(rd, 1),
                                      "write_only": round(wr, 1)}
+        log("mixed-stream probe at the chunk's read and write bytes (bf16 and FP8 output)")
+        mix = mix_probe_ceilings()
+        rec["probe_ceilings_gbs"]["mix_bf16"] = mix["bf16"]["gbs"]
+        rec["probe_ceilings_gbs"]["mix_fp8"] = mix["fp8"]["gbs"]
+        rec["mix_probe"] = mix
+        rec["mix_probe"]["headline_of_mix"] = round(gbs / mix["bf16"]["gbs"], 4)
         log("decode latency, T = 1..64 (H=6144, K=8), graph-replayed, same and fresh inputs")
         rec["decode_latency_us"] = decode_latency()
         log("512-token batch, cold and warm")
@@ -1241,6 +1414,8 @@ def run_bench(args):
         rec["dense_residual_rmsnorm"] = dense_figures()
         log("FP8 (E4M3 per-token) normalised output")
         rec["fp8_output"] = fp8_figures()
+        rec["mix_probe"]["fp8_of_mix"] = round(
+            rec["fp8_output"]["prefill_T8192"]["gbs"] / mix["fp8"]["gbs"], 4)
         log("dense residual add + RMSNorm with FP8 output")
         rec["dense_fp8_output"] = dense_fp8_figures()
         log("row layouts: random permutation against rows grouped by expert")
@@ -1729,6 +1904,10 @@ def main():
     ap.add_argument("--sweep-reps", type=int, default=3)
     ap.add_argument("--cold-table", action="store_true",
                     help="µs per call against T (fused, FP8-output, dense), fresh inputs")
+    ap.add_argument("--mix-sweep", action="store_true",
+                    help="depth x residency sweep of the mixed-stream probe (JSON)")
+    ap.add_argument("--summarize-mix", default="",
+                    help="a --mix-sweep record to write as a markdown summary (--out)")
     ap.add_argument("--summarize-cold", default="",
                     help="stdout of bench.py --cold-table: write it as a profiles/ table")
     ap.add_argument("--sweep-h", type=int, default=6144,
@@ -1784,6 +1963,9 @@ def main():
         return summarize_phases(args)
     if args.summarize_sweep:
         return summarize_sweep(args)
+    if args.summarize_mix:
+        summarize_mix(args)
+        return
     if args.summarize_cold:
         return summarize_cold(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1804,6 +1986,11 @@ def main():
         import torch
         torch.cuda.set_device(0)
         print(json.dumps({"cold_table": cold_table()}), flush=True)
+        return
+    if args.mix_sweep:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(mix_sweep()), flush=True)
         return
     if args.state_run:
         return run_states(args)

@@ -121,3 +121,35 @@ def test_env_log_reports_each_launch():
     assert len(lines) == 2, r.stderr[-2000:]
     assert "T=4 H=2048 K=8 variant=top8 out=bf16 path=token" in lines[0]
     assert "T=1024 H=2048 K=8 variant=top8 out=bf16 path=stream" in lines[1]
+
+
+def test_env_log_store_policy_follows_the_output_bytes():
+    """The automatic output stores: write-back on the token path and on the
+    stream path while both outputs together stay within 12 MiB, write-through
+    above that (T = 512 and 513 at H = 6144, 1536 and 1537 at H = 2048). Read
+    from the launch log of a child process."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import torch, synth\n"
+            "from tests import gpu_util as gu\n"
+            "for T, H in ((511, 6144), (512, 6144), (513, 6144), (1536, 2048), (1537, 2048)):\n"
+            "    d = synth.generate(T, H, 8, seed=6)\n"
+            "    gu.run(gu.to_device(d), d['eps'], d['scale'])\n"
+            "torch.cuda.synchronize()\n")
+    env = dict(os.environ, MFR_LOG="1")
+    env.pop("MFR_PATH", None)
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("moe_finalize_rmsnorm: T=")]
+    assert len(lines) == 5, r.stderr[-2000:]
+    want = (("T=511 H=6144", "path=token", "stores=write-back"),
+            ("T=512 H=6144", "path=stream", "stores=write-back"),
+            ("T=513 H=6144", "path=stream", "stores=write-through"),
+            ("T=1536 H=2048", "path=stream", "stores=write-back"),
+            ("T=1537 H=2048", "path=stream", "stores=write-through"))
+    for ln, parts in zip(lines, want):
+        for part in parts:
+            assert part in ln, (part, ln)
