@@ -120,15 +120,26 @@ constexpr float kFltMax = 0x1.fffffep127f;
 // complete out of order, so any use of one waits for all that are in
 // flight: the scheduling barrier keeps every use below the last load, so
 // that the sixteen loads cost one round trip rather than one each.
+// The loads go through the constant address space: perm_idx and topk_w are
+// never written while a kernel runs (every entry point refuses outputs that
+// overlap them), and saying so keeps them scalar loads after a store, as in
+// the persistent kernel's loop. There, a compiler that must assume the
+// stores could change them emits vector loads instead, and vector loads and
+// stores share one in-order counter: waiting for the metadata then waits for
+// every store and row load issued before it, the next token's included.
 template <bool CHECK_K>
 __device__ __forceinline__ void load_meta8(const Params& p, const int32_t* prow, const float* wrow,
                                            int k0, int32_t (&idx)[8], float (&wr)[8]) {
+    typedef const int32_t __attribute__((address_space(4)))* const_i32;
+    typedef const float __attribute__((address_space(4)))* const_f32;
+    const const_i32 prow_c = (const_i32)prow;
+    const const_f32 wrow_c = (const_f32)wrow;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
         const int k = k0 + kk;
         const int kc = CHECK_K ? (k < p.K ? k : p.K - 1) : k;
-        idx[kk] = prow[kc];
-        wr[kk] = wrow[kc];
+        idx[kk] = prow_c[kc];
+        wr[kk] = wrow_c[kc];
     }
     if constexpr (CHECK_K) __builtin_amdgcn_sched_barrier(0);
 }
