@@ -1051,18 +1051,19 @@ def _sweep(workloads, shapes, reps, phases, H=6144):
     return out
 
 
-def sweep_shapes(reps=3, cold_bytes=600_000_000, phases=None, ts=SWEEP_TS):
-    """Every launch shape at the fused op's workload sizes (H = 6144, K = 8):
-    the one-token-per-workgroup kernel at 1..4 vectors per thread (768, 384,
-    256 and 192 threads) with write-back and write-through stores, and the
-    persistent kernel with both store policies, beside the automatic choice,
-    in the HBM-cold harness of _sweep_workloads. The token and stream paths
-    are automatic choices among these shapes.
+def sweep_shapes(reps=3, cold_bytes=600_000_000, phases=None, ts=SWEEP_TS, H=6144):
+    """Every launch shape at the fused op's workload sizes (K = 8; H = 6144
+    unless asked otherwise): the one-token-per-workgroup kernel at 1..4
+    vectors per thread (at H = 6144: 768, 384, 256 and 192 threads) with
+    write-back and write-through stores, and the persistent kernel with both
+    store policies, beside the automatic choice, in the HBM-cold harness of
+    _sweep_workloads. The token and stream paths are automatic choices among
+    these shapes.
 
     With phases (a list), the calls are launched eagerly instead (see
     _sweep)."""
-    res = _sweep(_sweep_workloads(ts, cold_bytes), _shape_list(), reps, phases)
-    return {"kind": "shapes", "H": 6144, "K": 8, "unit": "us", "reps": reps, "T": res}
+    res = _sweep(_sweep_workloads(ts, cold_bytes, H=H), _shape_list(), reps, phases, H=H)
+    return {"kind": "shapes", "H": H, "K": 8, "unit": "us", "reps": reps, "T": res}
 
 
 def sweep_alternatives(reps=5, cold_bytes=600_000_000, phases=None, ts=ALT_TS, H=6144,
@@ -1083,9 +1084,9 @@ def run_sweep(args):
     alt = args.alternatives
     default_ts = ALT_TS if alt else SWEEP_TS
     ts = tuple(int(x) for x in args.sweep_ts.split(",")) if args.sweep_ts else default_ts
-    kw = dict(reps=args.sweep_reps, ts=ts)
+    kw = dict(reps=args.sweep_reps, ts=ts, H=args.sweep_h)
     if alt:
-        fn, kw["H"], kw["mode"] = sweep_alternatives, args.sweep_h, args.sweep_mode
+        fn, kw["mode"] = sweep_alternatives, args.sweep_mode
     else:
         fn = sweep_shapes
     if args.eager:
@@ -1911,7 +1912,7 @@ def main():
     ap.add_argument("--summarize-cold", default="",
                     help="stdout of bench.py --cold-table: write it as a profiles/ table")
     ap.add_argument("--sweep-h", type=int, default=6144,
-                    help="with --shape-sweep --alternatives: the hidden size")
+                    help="with --shape-sweep: the hidden size")
     ap.add_argument("--sweep-mode", default="bf16", choices=("bf16", "fp8", "dense"),
                     help="with --shape-sweep --alternatives: the fused op, its FP8-output form "
                          "or the dense tail")
