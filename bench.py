@@ -1401,6 +1401,8 @@ def run_bench(args):
         cp, rd, wr = probe_ceilings()
         rec["probe_ceilings_gbs"] = {"copy": round(cp, 1), "read_only": round(rd, 1),
                                      "write_only": round(wr, 1)}
+        # the headline against the copy kernel's ceiling of the same run
+        rec["headline_of_copy_ceiling"] = round(gbs / cp, 4)
         log("mixed-stream probe at the chunk's read and write bytes (bf16 and FP8 output)")
         mix = mix_probe_ceilings()
         rec["probe_ceilings_gbs"]["mix_bf16"] = mix["bf16"]["gbs"]
