@@ -115,7 +115,8 @@ enum mfr_status {
  * between workgroup shapes (their reduction trees differ). */
 enum mfr_path {
     MFR_PATH_UNSUPPORTED = 0,
-    MFR_PATH_TOKEN = 1,   /* small T, latency: widest workgroup per token (768 threads at H = 6144) */
+    MFR_PATH_TOKEN = 1,   /* small T, latency: widest workgroup per token (768 threads at H = 6144),
+                             write-through bf16 stores up to T = 64 */
     MFR_PATH_STREAM = 2,  /* large T, bandwidth: 256 threads per token, write-through stores once
                              the outputs pass 12 MiB */
     MFR_PATH_PERSIST = 3  /* large T, bandwidth: persistent multi-token workgroups, two tokens in

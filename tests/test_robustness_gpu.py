@@ -124,8 +124,10 @@ def test_env_log_reports_each_launch():
 
 
 def test_env_log_store_policy_follows_the_output_bytes():
-    """The automatic output stores: write-back on the token path and on the
-    stream path while both outputs together stay within 12 MiB, write-through
+    """The automatic output stores: write-through on the token path up to 64
+    tokens with bf16 output and write-back above (T = 64 and 65) or with FP8
+    output (T = 28), write-back on the stream
+    path while both outputs together stay within 12 MiB and write-through
     above that (T = 512 and 513 at H = 6144, 1536 and 1537 at H = 2048). Read
     from the launch log of a child process."""
     import os
@@ -134,9 +136,13 @@ def test_env_log_store_policy_follows_the_output_bytes():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     code = ("import torch, synth\n"
             "from tests import gpu_util as gu\n"
-            "for T, H in ((511, 6144), (512, 6144), (513, 6144), (1536, 2048), (1537, 2048)):\n"
+            "for T, H in ((64, 6144), (65, 6144), (511, 6144), (512, 6144), (513, 6144),\n"
+            "             (1536, 2048), (1537, 2048)):\n"
             "    d = synth.generate(T, H, 8, seed=6)\n"
             "    gu.run(gu.to_device(d), d['eps'], d['scale'])\n"
+            "from tests.test_fp8_gpu import run_fp8\n"
+            "d = synth.generate(28, 6144, 8, seed=6)\n"
+            "run_fp8(gu.to_device(d), d)\n"
             "torch.cuda.synchronize()\n")
     env = dict(os.environ, MFR_LOG="1")
     env.pop("MFR_PATH", None)
@@ -144,12 +150,15 @@ def test_env_log_store_policy_follows_the_output_bytes():
                        text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stderr.splitlines() if ln.startswith("moe_finalize_rmsnorm: T=")]
-    assert len(lines) == 5, r.stderr[-2000:]
-    want = (("T=511 H=6144", "path=token", "stores=write-back"),
+    assert len(lines) == 8, r.stderr[-2000:]
+    want = (("T=64 H=6144", "path=token", "stores=write-through"),
+            ("T=65 H=6144", "path=token", "stores=write-back"),
+            ("T=511 H=6144", "path=token", "stores=write-back"),
             ("T=512 H=6144", "path=stream", "stores=write-back"),
             ("T=513 H=6144", "path=stream", "stores=write-through"),
             ("T=1536 H=2048", "path=stream", "stores=write-back"),
-            ("T=1537 H=2048", "path=stream", "stores=write-through"))
+            ("T=1537 H=2048", "path=stream", "stores=write-through"),
+            ("T=28 H=6144", "out=fp8 path=token", "stores=write-back"))
     for ln, parts in zip(lines, want):
         for part in parts:
             assert part in ln, (part, ln)

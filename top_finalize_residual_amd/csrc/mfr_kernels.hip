@@ -788,6 +788,18 @@ constexpr int64_t kTokenPathMaxT = 511;
 // 768, 3-5% from 2048), where the grid's last tokens run alone and written-
 // back outputs would wait in the L2 for the end of the kernel.
 constexpr uint64_t kWriteThroughAboveBytes = 12ull << 20;
+// Token counts up to which the token path writes its bf16 outputs through
+// too. Measured on MI355X at H = 6144 (decode harnesses, interleaved): at
+// T = 1 to 64 write-through is 0.6-3% faster for the fused op with fresh
+// inputs, with the same inputs re-read and right after a producer wrote the
+// rows, and level to 4% faster for the dense tail; at T = 128 write-back is
+// 1-2% ahead. The same holds at H = 4096 and 7168 (HBM-cold sweeps, 1-2.5%
+// at T = 1, 28 and 64). With one token per CU the call ends with every
+// output line written; written-back lines would still be in the L2 then,
+// waiting for the end of the kernel. The FP8 output (codes and a four-byte
+// scale per token) is 0.1-3.5% slower written through, so it keeps
+// write-back.
+constexpr int64_t kTokenWriteThroughMaxT = 64;
 // The stream path's 256-thread, 3-vector kernels of the fused op with bf16
 // or FP8 output (3 workgroups per CU by their registers) run with at most
 // kCapPerCu workgroups per CU from kCapMinT tokens on, for H above kCapMinH
@@ -924,9 +936,9 @@ int store_policy(int path, int64_t T, int64_t H, Variant v, int qm) {
     if ((f == MFR_STORE_NONTEMPORAL || f == MFR_STORE_NONTEMPORAL_WRITE_THROUGH) && v == kTop8 &&
         qm == mfr::kOutBf16 && path != MFR_PATH_PERSIST)
         return f == MFR_STORE_NONTEMPORAL ? kStoreNt : kStoreNtWt;
-    return path != MFR_PATH_TOKEN && static_cast<uint64_t>(T) * H * 4 > kWriteThroughAboveBytes
-               ? kStoreWt
-               : kStoreWb;
+    if (path == MFR_PATH_TOKEN)
+        return T <= kTokenWriteThroughMaxT && qm == mfr::kOutBf16 ? kStoreWt : kStoreWb;
+    return static_cast<uint64_t>(T) * H * 4 > kWriteThroughAboveBytes ? kStoreWt : kStoreWb;
 }
 
 bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {

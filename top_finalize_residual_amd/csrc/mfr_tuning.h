@@ -17,8 +17,9 @@
 extern "C" {
 #endif
 
-/* Cache policy of the output stores. AUTO writes back outputs that fit in
- * the L2 and writes larger ones through (sc1). The two non-temporal
+/* Cache policy of the output stores. AUTO writes through (sc1) once both
+ * outputs pass 12 MiB, and at decode sizes (up to 64 tokens) when the output
+ * is bf16; otherwise it writes back. The two non-temporal
  * encodings (nt, and nt with sc1) exist for the fused op with exactly eight
  * slots and bf16 output, on the grid paths; any other launch takes the
  * automatic policy instead. */
