@@ -288,13 +288,15 @@ def probe_ceilings(nbytes=1 << 30, reps=10):
 
 # The mixed-stream probe at the headline chunk's bytes: its reads (rows,
 # shared and residual) against its writes with bf16 output, or with FP8 codes
-# (residual_out plus one byte per element). Per thread and unit of work: 30
-# vectors read for 6 written is one token at 256 threads with bf16 output;
-# 20 for 3 the FP8 proportion.
-MIX_PAIRS = {"bf16": (30, 6), "fp8": (20, 3)}
+# (residual_out plus one byte per element). Per thread and unit of work, each
+# one token of the fused op at 256 threads: 30 vectors read for 6 written
+# with bf16 output; 30 read for 3 written and three 8-byte stores to a
+# second region (the codes form) with FP8 output.
+MIX_WT, MIX_PIPE, MIX_CODES = 1, 2, 4  # mfr_mix_probe flags
+MIX_PAIRS = {"bf16": (30, 6), "fp8": (30, 3)}
+MIX_FORM = {"bf16": 0, "fp8": MIX_CODES}
 MIX_READ_BYTES = 8192 * 8 * 6144 * 2 + 2 * 8192 * 6144 * 2  # rows, shared, residual
 MIX_WRITE_BYTES = {"bf16": 2 * 8192 * 6144 * 2, "fp8": 8192 * 6144 * 3}
-MIX_WT, MIX_PIPE = 1, 2  # mfr_mix_probe flags
 
 
 class _MixProbe:
@@ -314,7 +316,8 @@ class _MixProbe:
         import ctypes
         import torch
         rb, wb = ctypes.c_int64(0), ctypes.c_int64(0)
-        wbytes = MIX_WRITE_BYTES["fp8" if reads * 3 == writes * 20 else "bf16"]
+        fp8 = bool(flags & MIX_CODES) or reads * 3 == writes * 20
+        wbytes = MIX_WRITE_BYTES["fp8" if fp8 else "bf16"]
         rc = []
 
         def call():
@@ -341,8 +344,9 @@ class _MixProbe:
 
 def mix_probe_ceilings(reps=10):
     """GB/s (read + write bytes) of the mixed-stream probe at the headline
-    chunk's own byte counts, with bf16 output and with FP8 codes, in the
-    headline's cache state (one buffer set, calls back to back). Best over
+    chunk's own byte counts, with bf16 output and with FP8 codes (each in
+    units of one token of the fused op), in the headline's cache state (one
+    buffer set, calls back to back). Best over
     write-back and write-through stores and four launch shapes: one workgroup
     per unit of work (as the fused op launches one per token), the same capped
     at 2 workgroups per CU through reserved LDS (as the fused op at this
@@ -356,7 +360,7 @@ def mix_probe_ceilings(reps=10):
         for wt in (0, MIX_WT):
             for grid, per_cu, shape in ((0, 0, "per-unit"), (0, 2, "per-unit-cap2"),
                                         (2 * cus, 0, "2-per-cu"), (8 * cus, 0, "8-per-cu")):
-                r = probe.gbs_us(a, b, wt, grid, per_cu, reps)
+                r = probe.gbs_us(a, b, wt | MIX_FORM[mode], grid, per_cu, reps)
                 if r is None:
                     continue
                 detail[f"{'wt' if wt else 'wb'}-{shape}"] = [round(r[0], 1), round(r[1], 2)]
@@ -378,8 +382,9 @@ def mix_sweep(reps=3):
     """Median GB/s over reps interleaved repetitions of every depth x
     residency of the mixed-stream probe (bf16 proportion, write-through
     stores), the one-unit form with no cap, and the FP8 proportion at its
-    two depths; keys "unit/A<reads>/cap<n>", "pipe/A<reads>/<n>-per-cu",
-    "unit/A<reads>/nocap" and "fp8/A<reads>/cap<n>"."""
+    two depths and in the FP8-code form (one token with FP8 output); keys
+    "unit/A<reads>/cap<n>", "pipe/A<reads>/<n>-per-cu", "unit/A<reads>/nocap",
+    "fp8/A<reads>/cap<n>" and "fp8codes/A30/cap<n>"."""
     import statistics
     probe = _MixProbe()
     runs = {}
@@ -399,6 +404,10 @@ def mix_sweep(reps=3):
                 r = probe.gbs_us(a, b, MIX_WT, 0, n)
                 if r is not None:
                     runs.setdefault(f"fp8/A{a}/cap{n}", []).append(r[0])
+        for n in (1, 2, 3):
+            r = probe.gbs_us(30, 3, MIX_WT | MIX_CODES, 0, n)
+            if r is not None:
+                runs.setdefault(f"fp8codes/A30/cap{n}", []).append(r[0])
         log(f"mix sweep: repetition {rep + 1} of {reps}")
     probe.close()
     return {k: round(statistics.median(v), 1) for k, v in runs.items()}
@@ -431,12 +440,15 @@ def mix_sweep_lines(path):
         row = [rec.get(f"pipe/A{a}/{n}-per-cu") for n in MIX_CAPS]
         lines.append(f"| {a} ({a * 4}) | " + " | ".join("—" if v is None else f"{v:,.0f}"
                                                          for v in row) + " |")
-    lines += ["", "FP8 proportion (A read for 3A/20 written), one unit per workgroup:", "",
+    lines += ["", "FP8 proportion (A read for 3A/20 written), one unit per workgroup; the codes "
+              "form is one token with FP8 output (30 read, then 3 vectors and 3 half vectors "
+              "written, the halves to a region of their own):", "",
               "| A (KiB per unit) | n = 1 | n = 2 | n = 3 |", "|---|---|---|---|"]
-    for a in (20, 40):
-        row = [rec.get(f"fp8/A{a}/cap{n}") for n in (1, 2, 3)]
-        lines.append(f"| {a} ({a * 4}) | " + " | ".join("—" if v is None else f"{v:,.0f}"
-                                                         for v in row) + " |")
+    for a, key in ((20, "fp8/A20"), (40, "fp8/A40"), (30, "fp8codes/A30")):
+        row = [rec.get(f"{key}/cap{n}") for n in (1, 2, 3)]
+        name = f"{a} ({a * 4}), codes form" if key.startswith("fp8codes") else f"{a} ({a * 4})"
+        lines.append(f"| {name} | " + " | ".join("—" if v is None else f"{v:,.0f}"
+                                                  for v in row) + " |")
     return lines
 
 

@@ -354,21 +354,25 @@ def test_sweep_and_cold_tables(tmp_path):
 
 def test_mix_probe_byte_counts_and_refusals():
     """The mixed-stream probe's buffers are the headline chunk's own read and
-    write bytes, in whole units of both proportions; the probe refuses an
-    uninstantiated proportion, bad flags, misaligned or missing buffers,
-    buffers below one unit and a pipelined launch with no grid before any
-    launch (so this runs without a GPU)."""
+    write bytes, in whole units of one token in both output forms; the probe
+    refuses an uninstantiated proportion, the FP8-code form on any pair but
+    (30, 3) and that pair without it, bad flags, misaligned or missing
+    buffers, buffers below one unit and a pipelined launch with no grid
+    before any launch (so this runs without a GPU)."""
     import ctypes
     H, T, K = 6144, 8192, 8
     assert bench.MIX_READ_BYTES == (T * K + 2 * T) * H * 2
     assert bench.MIX_WRITE_BYTES["bf16"] == 2 * T * H * 2
     assert bench.MIX_WRITE_BYTES["fp8"] == T * H * 2 + T * H
     for mode, (a, b) in bench.MIX_PAIRS.items():
-        unit_r, unit_w = a * 256 * 16, b * 256 * 16
+        unit_r = a * 256 * 16
+        unit_w = b * 256 * (24 if bench.MIX_FORM[mode] & bench.MIX_CODES else 16)
         assert bench.MIX_READ_BYTES % unit_r == 0 and bench.MIX_WRITE_BYTES[mode] % unit_w == 0
-        assert bench.MIX_READ_BYTES // unit_r == bench.MIX_WRITE_BYTES[mode] // unit_w
-    # one token at 256 threads: 8 rows + shared + residual = 30 vectors per thread in, 6 out
-    assert bench.MIX_PAIRS["bf16"] == (30, 6)
+        assert bench.MIX_READ_BYTES // unit_r == bench.MIX_WRITE_BYTES[mode] // unit_w == T
+    # one token at 256 threads: 8 rows + shared + residual = 30 vectors per thread in; out,
+    # 6 vectors (residual_out, normed_out), or 3 and 3 half vectors (residual_out, codes)
+    assert bench.MIX_PAIRS["bf16"] == (30, 6) and bench.MIX_FORM["bf16"] == 0
+    assert bench.MIX_PAIRS["fp8"] == (30, 3) and bench.MIX_FORM["fp8"] == bench.MIX_CODES
     lib = bench._probe_lib()
     rb, wb = ctypes.c_int64(0), ctypes.c_int64(0)
     ok = 1 << 20  # stands in for a 16-byte aligned device address; never dereferenced here
@@ -379,7 +383,11 @@ def test_mix_probe_byte_counts_and_refusals():
     big = (ok, 1 << 30, ok + (1 << 30), 1 << 28)
     assert call(*big, reads=30, writes=5) == 1        # not an instantiated proportion
     assert call(*big, reads=35, writes=7) == 1
-    assert call(*big, flags=4) == 1 and call(*big, flags=-1) == 1
+    assert call(*big, flags=4) == 1 and call(*big, flags=8) == 1 and call(*big, flags=-1) == 1
+    assert call(*big, reads=30, writes=3) == 1        # (30, 3) only in the FP8-code form
+    assert call(*big, reads=20, writes=3, flags=4) == 1
+    assert call(ok, 1 << 30, ok + (1 << 30), 3 * 4096 * 3 // 2 - 16, reads=30, writes=3,
+                flags=4) == 1                         # below one unit of both regions
     assert call(*big, flags=2) == 1                   # pipelined needs a grid
     assert call(None, 1 << 30, ok, 1 << 28) == 1      # missing buffer
     assert call(ok + 8, 1 << 30, ok, 1 << 28) == 1    # misaligned
@@ -396,10 +404,11 @@ def test_mix_sweep_summary(tmp_path):
     del rec["unit/A40/cap4"]
     rec.update({f"unit/A{a}/nocap": 7.0 for a in bench.MIX_DEPTHS})
     rec.update({f"pipe/A{a}/{n}-per-cu": 9.0 for a in bench.MIX_DEPTHS for n in bench.MIX_CAPS})
-    rec.update({"fp8/A20/cap1": 6001.0, "fp8/A40/cap2": 6002.0})
+    rec.update({"fp8/A20/cap1": 6001.0, "fp8/A40/cap2": 6002.0, "fp8codes/A30/cap3": 6003.0})
     path = tmp_path / "mix.json"
     path.write_text(json.dumps(rec))
     lines = bench.mix_sweep_lines(str(path))
     assert "| 30 (120) | 1,030 | 2,030 | 3,030 | 4,030 | 7 |" in lines
     assert "| 40 (160) | 1,040 | 2,040 | 3,040 | — | 7 |" in lines
     assert "| 20 (80) | 6,001 | — | — |" in lines and "| 40 (160) | — | 6,002 | — |" in lines
+    assert "| 30 (120), codes form | — | — | 6,003 |" in lines

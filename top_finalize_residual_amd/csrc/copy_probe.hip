@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;  // 16-byte vectors in flight per thread per iteration
@@ -125,9 +126,26 @@ __device__ __forceinline__ void unit_stores(u32x4* dst, int64_t u, const u32x4 (
             x[j], rd, static_cast<int>((j * kThreads + threadIdx.x) * 16u), 0, AUX);
 }
 
-template <int A, int B, int AUX>
+// The FP8-code form's second output: per thread and unit, B 8-byte stores
+// (the two halves of each written vector folded together) into a region of
+// its own, as the FP8 codes (one byte per element) sit beside residual_out
+// (two bytes per element) in a buffer of their own.
+template <int B, int AUX>
+__device__ __forceinline__ void unit_stores8(u32x2* dst8, int64_t u, const u32x4 (&x)[B]) {
+    const rsrc_t rd = unit_rsrc(dst8 + u * (B * kThreads), B * kThreads * 8u);
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            u32x2{x[j].x ^ x[j].z, x[j].y ^ x[j].w}, rd,
+            static_cast<int>((j * kThreads + threadIdx.x) * 8u), 0, AUX);
+}
+
+// CODES: the B 16-byte stores of each unit are followed by B 8-byte stores
+// into dst8 (null otherwise).
+template <int A, int B, int AUX, bool CODES>
 __global__ __launch_bounds__(kThreads) void mfr_mix_probe_kernel(const u32x4* __restrict__ src,
                                                                  u32x4* __restrict__ dst,
+                                                                 u32x2* __restrict__ dst8,
                                                                  int64_t units) {
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
         u32x4 v[A];
@@ -136,12 +154,14 @@ __global__ __launch_bounds__(kThreads) void mfr_mix_probe_kernel(const u32x4* __
         u32x4 x[B];
         unit_fold<A, B>(v, x);
         unit_stores<B, AUX>(dst, u, x);
+        if constexpr (CODES) unit_stores8<B, AUX>(dst8, u, x);
     }
 }
 
-template <int A, int B, int AUX>
+template <int A, int B, int AUX, bool CODES>
 __global__ __launch_bounds__(kThreads) void mfr_mix_pipe_probe_kernel(const u32x4* __restrict__ src,
                                                                       u32x4* __restrict__ dst,
+                                                                      u32x2* __restrict__ dst8,
                                                                       int64_t units) {
     int64_t u = blockIdx.x;
     if (u >= units) return;
@@ -153,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void mfr_mix_pipe_probe_kernel(const u32x
         const int64_t next = u + gridDim.x;
         if (next < units) unit_loads<A>(src, next, v);
         unit_stores<B, AUX>(dst, u, x);
+        if constexpr (CODES) unit_stores8<B, AUX>(dst8, u, x);
     }
 }
 
@@ -214,7 +235,11 @@ extern "C" int mfr_write_probe(void* dst, int64_t bytes, uint32_t pattern, int g
 // output ((30, 6) is one token of it at 256 threads: 8 rows, shared and
 // residual in, residual_out and normed_out out), or (20, 3) and (40, 6),
 // twenty to three as with FP8 codes. flags: bit 0 writes through (else
-// back), bit 1 selects the pipelined form (which needs grid > 0). As many
+// back), bit 1 selects the pipelined form (which needs grid > 0), bit 2 the
+// FP8-code form, pair (30, 3) only: after its three 16-byte vectors each
+// thread writes three 8-byte ones, to a second region that starts where the
+// units' 16-byte writes end (one token of the fused op with FP8 output at
+// 256 threads: residual_out and the codes, twenty to three as well). As many
 // whole units as both buffers hold are processed; `grid` workgroups of 256
 // threads, or one workgroup per unit when grid is 0. per_cu > 0 reserves
 // enough dynamic LDS at launch that at most that many workgroups fit on a CU
@@ -224,10 +249,12 @@ extern "C" int mfr_write_probe(void* dst, int64_t bytes, uint32_t pattern, int g
 // the launch failed, 3 if the residency cannot be set that way.
 namespace {
 
-template <int A, int B, int AUX, bool PIPE>
-int mix_launch(dim3 g, int per_cu, const u32x4* s, u32x4* d, int64_t units, hipStream_t stream) {
-    const void* kern = PIPE ? reinterpret_cast<const void*>(&mfr_mix_pipe_probe_kernel<A, B, AUX>)
-                            : reinterpret_cast<const void*>(&mfr_mix_probe_kernel<A, B, AUX>);
+template <int A, int B, int AUX, bool PIPE, bool CODES>
+int mix_launch(dim3 g, int per_cu, const u32x4* s, u32x4* d, u32x2* d8, int64_t units,
+               hipStream_t stream) {
+    const void* kern =
+        PIPE ? reinterpret_cast<const void*>(&mfr_mix_pipe_probe_kernel<A, B, AUX, CODES>)
+             : reinterpret_cast<const void*>(&mfr_mix_probe_kernel<A, B, AUX, CODES>);
     size_t lds = 0;
     if (per_cu > 0) {
         int dev = 0, lds_cu = 0, fit = 0;
@@ -241,22 +268,23 @@ int mix_launch(dim3 g, int per_cu, const u32x4* s, u32x4* d, int64_t units, hipS
             fit != per_cu)
             return 3;
     }
-    void* args[] = {&s, &d, &units};
+    void* args[] = {&s, &d, &d8, &units};
     return hipLaunchKernel(kern, g, dim3(kThreads), args, lds, stream) == hipSuccess ? 0 : 2;
 }
 
-template <int A, int B>
-int mix_pick(int flags, dim3 g, int per_cu, const u32x4* s, u32x4* d, int64_t units,
+template <int A, int B, bool CODES = false>
+int mix_pick(int flags, dim3 g, int per_cu, const u32x4* s, u32x4* d, u32x2* d8, int64_t units,
              hipStream_t stream) {
-    switch (flags) {
-        case 0: return mix_launch<A, B, 0, false>(g, per_cu, s, d, units, stream);
-        case 1: return mix_launch<A, B, 16, false>(g, per_cu, s, d, units, stream);
-        case 2: return mix_launch<A, B, 0, true>(g, per_cu, s, d, units, stream);
-        default: return mix_launch<A, B, 16, true>(g, per_cu, s, d, units, stream);
+    switch (flags & 3) {
+        case 0: return mix_launch<A, B, 0, false, CODES>(g, per_cu, s, d, d8, units, stream);
+        case 1: return mix_launch<A, B, 16, false, CODES>(g, per_cu, s, d, d8, units, stream);
+        case 2: return mix_launch<A, B, 0, true, CODES>(g, per_cu, s, d, d8, units, stream);
+        default: return mix_launch<A, B, 16, true, CODES>(g, per_cu, s, d, d8, units, stream);
     }
 }
 
-bool mix_pair_ok(int a, int b) {
+bool mix_pair_ok(int a, int b, bool codes) {
+    if (codes) return a == 30 && b == 3;
     return (b * 5 == a && (a == 10 || a == 15 || a == 20 || a == 25 || a == 30 || a == 40)) ||
            (a == 20 && b == 3) || (a == 40 && b == 6);
 }
@@ -266,12 +294,15 @@ bool mix_pair_ok(int a, int b) {
 extern "C" int mfr_mix_probe(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
                              int reads, int writes, int flags, int grid, int per_cu,
                              int64_t* read_out, int64_t* write_out, hipStream_t stream) {
-    if (!src || !dst || src_bytes < 0 || dst_bytes < 0 || grid < 0 || flags < 0 || flags > 3 ||
-        per_cu < 0 || per_cu > 32 || !mix_pair_ok(reads, writes) || ((flags & 2) && grid == 0))
+    const bool codes = (flags & 4) != 0;
+    if (!src || !dst || src_bytes < 0 || dst_bytes < 0 || grid < 0 || flags < 0 || flags > 7 ||
+        per_cu < 0 || per_cu > 32 || !mix_pair_ok(reads, writes, codes) ||
+        ((flags & 2) && grid == 0))
         return 1;
     if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return 1;
     const int64_t ru = static_cast<int64_t>(reads) * kThreads * 16;
-    const int64_t wu = static_cast<int64_t>(writes) * kThreads * 16;
+    const int64_t w16 = static_cast<int64_t>(writes) * kThreads * 16;
+    const int64_t wu = codes ? w16 + w16 / 2 : w16;
     const int64_t units = src_bytes / ru < dst_bytes / wu ? src_bytes / ru : dst_bytes / wu;
     if (units <= 0 || units > 0x7FFFFFFF) return 1;
     if (read_out) *read_out = units * ru;
@@ -279,15 +310,18 @@ extern "C" int mfr_mix_probe(const void* src, int64_t src_bytes, void* dst, int6
     const dim3 g(static_cast<uint32_t>(grid == 0 ? units : grid));
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
+    // the second region starts at units * w16, a multiple of 16 bytes
+    u32x2* d8 = codes ? reinterpret_cast<u32x2*>(static_cast<char*>(dst) + units * w16) : nullptr;
+    if (codes) return mix_pick<30, 3, true>(flags, g, per_cu, s, d, d8, units, stream);
     switch (reads * 100 + writes) {
-        case 1002: return mix_pick<10, 2>(flags, g, per_cu, s, d, units, stream);
-        case 1503: return mix_pick<15, 3>(flags, g, per_cu, s, d, units, stream);
-        case 2004: return mix_pick<20, 4>(flags, g, per_cu, s, d, units, stream);
-        case 2505: return mix_pick<25, 5>(flags, g, per_cu, s, d, units, stream);
-        case 3006: return mix_pick<30, 6>(flags, g, per_cu, s, d, units, stream);
-        case 4008: return mix_pick<40, 8>(flags, g, per_cu, s, d, units, stream);
-        case 2003: return mix_pick<20, 3>(flags, g, per_cu, s, d, units, stream);
-        default: return mix_pick<40, 6>(flags, g, per_cu, s, d, units, stream);
+        case 1002: return mix_pick<10, 2>(flags, g, per_cu, s, d, d8, units, stream);
+        case 1503: return mix_pick<15, 3>(flags, g, per_cu, s, d, d8, units, stream);
+        case 2004: return mix_pick<20, 4>(flags, g, per_cu, s, d, d8, units, stream);
+        case 2505: return mix_pick<25, 5>(flags, g, per_cu, s, d, d8, units, stream);
+        case 3006: return mix_pick<30, 6>(flags, g, per_cu, s, d, d8, units, stream);
+        case 4008: return mix_pick<40, 8>(flags, g, per_cu, s, d, d8, units, stream);
+        case 2003: return mix_pick<20, 3>(flags, g, per_cu, s, d, d8, units, stream);
+        default: return mix_pick<40, 6>(flags, g, per_cu, s, d, d8, units, stream);
     }
 }
 
