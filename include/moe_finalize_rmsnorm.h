@@ -165,7 +165,11 @@ int moe_finalize_rmsnorm_checked(const uint16_t* expert_out, int64_t R,
  *   normed_fp8[t,h]  = E4M3(y[h] * 448 / amax)   (OCP E4M3: bias 7, 3 mantissa
  *                      bits, round to nearest even, saturated to +-448)
  *
- * so y[h] ~= value(normed_fp8[t,h]) * fp8_scale[t]. Arguments as for
+ * so y[h] ~= value(normed_fp8[t,h]) * fp8_scale[t]. The library forms the two
+ * quotients with the hardware reciprocal, each within 2^-20 relative, the
+ * factor 448 / amax rounded low, so that no code passes 448: a code can then
+ * differ from that of the exact quotient only where y[h] * 448 / amax lies
+ * within that distance of the midpoint between two codes. Arguments as for
  * moe_finalize_rmsnorm, plus:
  *   normed_out   [T, H] bf16   optional: NULL skips the bf16 normed output
  *   normed_fp8   [T, H] uint8  E4M3 codes, 8-byte aligned

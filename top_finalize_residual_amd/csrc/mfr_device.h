@@ -84,15 +84,20 @@ __device__ __forceinline__ void buf_store_u32(uint32_t v, rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, AUX);
 }
 
-// 448 / m for m > 0, made safe to scale by: the correctly rounded quotient,
-// lowered by one ulp where m times it rounds above 448. Rounding is monotone,
-// so |x| <= m then gives |x * factor| <= 448 after rounding, the largest
-// finite OCP E4M3 magnitude (the hardware conversion turns values above it
-// into NaN). m = +inf gives 0.
+// 1/448 rounded to fp32, and 1 - 2^-21 (exact in fp32).
+constexpr float kInvE4m3Max = 1.0f / 448.0f;
+constexpr float kE4m3Shrink = 1.0f - 0x1p-21f;
+
+// 448 / m for m in [2^-90, 2^128] or +inf, made safe to scale by: the
+// hardware reciprocal (v_rcp_f32, within 1 ulp) of m * RN(1/448), shrunk by
+// 2^-21. Whatever the three roundings do (each within 2^-24 or 2^-23
+// relative), m times the factor stays below 448 * (1 - 2^-23), and the factor
+// is within 2^-20 of 448 / m. Rounding is monotone, so |x| <= m then gives
+// |x * factor| <= 448 after rounding, the largest finite OCP E4M3 magnitude
+// (the hardware conversion turns values above it into NaN). Over that range
+// of m every intermediate is a normal number. m = +inf gives 0.
 __device__ __forceinline__ float e4m3_factor(float m) {
-    float f = 448.0f / m;
-    if (m * f > 448.0f) f = __uint_as_float(__float_as_uint(f) - 1u);
-    return f;
+    return __builtin_amdgcn_rcpf(m * kInvE4m3Max) * kE4m3Shrink;
 }
 
 // Eight fp32 values in [-448, 448] (or NaN) to eight OCP E4M3 codes in

@@ -65,7 +65,7 @@ struct Params {
     float eps;
     float scale;
     uint32_t rows;  // rows of expert_out, at most 2^31: an index at or past it is masked
-    float h_f;      // H as float (exact: H <= 16384)
+    float inv_h;    // 1 / H rounded to fp32: the mean of squares is their sum times it
     int64_t T;
     uint8_t* normed_fp8;  // [T, H] E4M3 codes (FP8 output modes only)
     float* fp8_scale;     // [T] per-token scales (FP8 output modes only)
@@ -75,7 +75,7 @@ struct Params {
     // (The order above serves the same end: a run of three used 32-bit
     // fields is loaded as four, and a register filled with an unused field
     // may be reused at once, which waits for the load. rows, used only by
-    // the checked kernels, therefore sits between scale and h_f.)
+    // the checked kernels, therefore sits between scale and inv_h.)
     int V;  // 16-byte vectors per row, H / 8
     int K;
 };
@@ -269,7 +269,7 @@ __device__ __forceinline__ void normalise_wide(const Params& p, const int64_t t,
     double tot = 0.0;
 #pragma unroll 1
     for (int w = 0; w < nw; ++w) tot += lds.red64[w];
-    const double rstd = 1.0 / __builtin_sqrt(tot / static_cast<double>(p.h_f) +
+    const double rstd = 1.0 / __builtin_sqrt(tot / (static_cast<double>(p.V) * 8.0) +
                                              static_cast<double>(p.eps));
     // rstd = m * 2^k; an infinite, zero or NaN rstd (an all-zero row with
     // eps = 0, an infinite or NaN s) is used as it is, as in the fp32 path.
@@ -410,7 +410,10 @@ __device__ __forceinline__ void finish_token(const Params& p, const int64_t t,
     float rmg = 0.0f;
 #pragma unroll
     for (int w = MAX_WAVES; w < NRED; ++w) rmg = __builtin_fmaxf(rmg, part[w]);
-    const float ms_eps = tot / p.h_f + p.eps;
+    // the mean of squares as a product with the rounded 1/H: within an ulp
+    // of the quotient, and a multiply instead of the division's sequence on
+    // the path from the barrier to the stores
+    const float ms_eps = tot * p.inv_h + p.eps;
 
     // residual_out = bf16(s), one rounding
     if constexpr (!EARLY_RO) {
@@ -458,18 +461,20 @@ __device__ __forceinline__ void finish_token(const Params& p, const int64_t t,
         // amax / 448, codes = E4M3(y * 448 / amax). Since rstd > 0 is common
         // to y and amax, y * 448 / amax = sg * (448 / max |sg|): one multiply
         // per element, with no rstd in it.
-        //   * The factor is rounded down by an ulp where max |sg| times it
-        //     exceeds 448, so (rounding being monotone) no element can pass
-        //     448 and the conversion needs no clamp.
-        //   * Rows with max |sg| < 2^-100, where 448 / max |sg| could
-        //     overflow, are scaled by 2^64 first (exact).
+        //   * The factor (e4m3_factor) is a reciprocal shrunk by 2^-21, so
+        //     that max |sg| times it stays below 448: no element can pass 448
+        //     and the conversion needs no clamp. The scale is amax times the
+        //     rounded 1/448. Both are within 2^-20 of the quotients, and
+        //     neither puts a division between the barrier and the stores.
+        //   * Rows with max |sg| < 2^-100, whose factor could overflow, are
+        //     scaled by 2^64 first (exact).
         //   * A row with amax = 0, or rstd NaN, 0 or infinite, keeps the
         //     direct form y * 0: codes 0, or NaN where y is NaN; scale 1.
         // NaN elements (a NaN gamma) stay NaN; the conversion maps them to
         // the NaN code.
         const float rmax = rmg * rstd;
         const bool zero_row = !(rmax > 0.0f);
-        const float qscale = zero_row ? 1.0f : rmax / kE4m3Max;
+        const float qscale = zero_row ? 1.0f : rmax * kInvE4m3Max;
         const rsrc_t q_r = make_rsrc(p.normed_fp8 + t * static_cast<int64_t>(p.V) * 8,
                                      static_cast<uint32_t>(p.V) * 8u);
         if (!zero_row && rmg >= 0x1p-100f) {
@@ -622,7 +627,7 @@ __global__ __launch_bounds__(Bound<VPT>::kThreads) void mfr_fused_kernel(
     q.T = p.T;
     q.eps = p.eps;
     q.scale = p.scale;
-    q.h_f = p.h_f;
+    q.inv_h = p.inv_h;
     q.rows = p.rows;
     q.normed_fp8 = p.normed_fp8;
     q.fp8_scale = p.fp8_scale;
@@ -1183,7 +1188,7 @@ mfr::Params from_token(const mfr::Params& p, int64_t t0) {
 // changes no result.
 int launch(mfr::Params& p, int64_t T, int64_t H, Variant v, int qm, hipStream_t stream) {
     p.T = T;
-    p.h_f = static_cast<float>(H);
+    p.inv_h = 1.0f / static_cast<float>(H);
     p.V = static_cast<int>(H / 8);
     int path = choose_path(T, H, v == kDense ? 1 : p.K);
     if (path == MFR_PATH_PERSIST && !persist_serves(v, qm))
