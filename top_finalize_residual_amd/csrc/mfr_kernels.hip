@@ -809,12 +809,12 @@ constexpr int64_t kTokenWriteThroughMaxT = 64;
 // or FP8 output (3 workgroups per CU by their registers) run with at most
 // kCapPerCu workgroups per CU from kCapMinT tokens on, for H above kCapMinH
 // (up to 6144, where those kernels end). Measured on MI355X, every
-// alternative interleaved, at H = 6144 in four sweeps: bf16 0.6-1.6% faster
+// alternative interleaved, at H = 6144 in five sweeps: bf16 0.6-1.9% faster
 // at T = 4096 and 8192, with one buffer set, with the Infinity Cache flushed
-// before each call and with alternating outputs alike, level to 0.4% faster
-// at 2048, and level at T = 512 and 1024; FP8 0.35-1.0% faster at T = 8192,
+// before each call and with alternating outputs alike, level to 0.7% faster
+// at 2048, and level at T = 512 and 1024; FP8 0.3-1.0% faster at T = 8192,
 // level to 1.2% faster at 2048 and 4096. At H = 5120 (bf16) level or mixed
-// (-1% to +2%) in three sweeps, so the rule stops above it. At H = 4096
+// (-1% to +2%) in four sweeps, so the rule stops above it. At H = 4096
 // (another kernel, 7 per CU) and for the dense tail (8 per CU) a cap of 2
 // was slower.
 constexpr int64_t kCapMinT = 2048;
