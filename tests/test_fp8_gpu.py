@@ -89,6 +89,13 @@ def check_fp8(codes, scales, ref, gamma, eps, abs_floor=None):
         v = scaled[diff == 1]
         assert np.all(np.abs(v - (a + b) / 2) <= tol[diff == 1]), "code differs away from a tie"
     assert not np.any((codes & 0x7F) == 0x7F), "NaN code"
+    # the element of largest magnitude of every row with a finite nonzero scale
+    # encodes to exactly +-448 (0x7E): the factor keeps it from passing 448, and
+    # no lower code is within a step of it
+    live = np.isfinite(want_scale) & (want_scale > 0) & (want_scale != 1.0)
+    if live.any():
+        top = (codes[live] & 0x7F).max(axis=1)
+        assert np.all(top == 0x7E), "row maximum not at 448"
     return want
 
 
