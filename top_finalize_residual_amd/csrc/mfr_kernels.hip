@@ -522,9 +522,10 @@ __device__ __forceinline__ void finalize_token(const Params& p, const int64_t t,
 #pragma unroll
     for (int j = 0; j < VPT; ++j) off[j] = static_cast<uint32_t>(tid + j * nt) * 16u;
 
-    // Order of issue: the routing metadata (scalar loads), then the loads that
-    // do not depend on it (shared, residual, gamma), and only then anything
-    // that waits for the metadata. The scheduling barrier keeps the compiler
+    // The routing metadata (scalar loads) and the loads that do not depend on
+    // it (shared, residual, gamma) are all in flight before anything that
+    // waits for the metadata; in the machine code the vector loads go out
+    // first, then the metadata. The scheduling barrier keeps the compiler
     // from sinking those independent loads below the metadata wait, so every
     // workgroup starts streaming HBM one memory latency earlier.
     constexpr bool DENSE = KT < 0;
