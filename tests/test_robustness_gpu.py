@@ -126,7 +126,8 @@ def test_env_log_reports_each_launch():
 def test_env_log_store_policy_follows_the_output_bytes():
     """The automatic output stores: write-through on the token path up to 64
     tokens with bf16 output and write-back above (T = 64 and 65) or with FP8
-    output (T = 28), write-back on the stream
+    output (T = 28), the dense tail alike (T = 28, bf16 and FP8 output),
+    write-back on the stream
     path while both outputs together stay within 12 MiB and write-through
     above that (T = 512 and 513 at H = 6144, 1536 and 1537 at H = 2048). Read
     from the launch log of a child process."""
@@ -143,6 +144,10 @@ def test_env_log_store_policy_follows_the_output_bytes():
             "from tests.test_fp8_gpu import run_fp8\n"
             "d = synth.generate(28, 6144, 8, seed=6)\n"
             "run_fp8(gu.to_device(d), d)\n"
+            "from tests.test_dense_gpu import run_dense, run_dense_fp8\n"
+            "d = synth.dense_inputs(28, 6144, seed=6)\n"
+            "run_dense(d)\n"
+            "run_dense_fp8(d, bf16_normed=False)\n"
             "torch.cuda.synchronize()\n")
     env = dict(os.environ, MFR_LOG="1")
     env.pop("MFR_PATH", None)
@@ -150,7 +155,7 @@ def test_env_log_store_policy_follows_the_output_bytes():
                        text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stderr.splitlines() if ln.startswith("moe_finalize_rmsnorm: T=")]
-    assert len(lines) == 8, r.stderr[-2000:]
+    assert len(lines) == 10, r.stderr[-2000:]
     want = (("T=64 H=6144", "path=token", "stores=write-through"),
             ("T=65 H=6144", "path=token", "stores=write-back"),
             ("T=511 H=6144", "path=token", "stores=write-back"),
@@ -158,7 +163,9 @@ def test_env_log_store_policy_follows_the_output_bytes():
             ("T=513 H=6144", "path=stream", "stores=write-through"),
             ("T=1536 H=2048", "path=stream", "stores=write-back"),
             ("T=1537 H=2048", "path=stream", "stores=write-through"),
-            ("T=28 H=6144", "out=fp8 path=token", "stores=write-back"))
+            ("T=28 H=6144", "out=fp8 path=token", "stores=write-back"),
+            ("T=28 H=6144", "variant=dense out=bf16 path=token", "stores=write-through"),
+            ("T=28 H=6144", "variant=dense out=fp8 path=token", "stores=write-back"))
     for ln, parts in zip(lines, want):
         for part in parts:
             assert part in ln, (part, ln)
